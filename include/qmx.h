@@ -1,0 +1,192 @@
+/*
+ * qmx.h -- C ABI of libqmx: group-wise affine quantized matrix-vector and
+ * small-M matrix multiply, and the Q8_0 / Q4_K block matvecs, for AMD MI355X
+ * (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument except those named "host" is a DEVICE pointer
+ *   owned by the caller.  The library never allocates, frees or copies
+ *   caller memory and never synchronises: work is enqueued on `stream`
+ *   (a hipStream_t; NULL means the default stream) and the call returns as
+ *   soon as it is enqueued.  Outputs are valid once the stream reaches them.
+ * - Arrays are dense and row-major.  `out` must not overlap any input.
+ * - All arguments are validated on the host before anything is enqueued; a
+ *   negative qmx_status is returned and nothing is launched when a check
+ *   fails.  QMX_ERR_LAUNCH reports a launch error returned by the HIP
+ *   runtime.  Empty problems (M == 0 or N == 0) return QMX_OK and launch
+ *   nothing; K == 0 writes zeros.
+ * - Results are bit-reproducible run to run for the same build, device,
+ *   arguments and split count: no atomics, fixed reduction orders.
+ * - Accumulation is float32 throughout; the output is rounded once, to
+ *   nearest even.
+ * - The library keeps no state between calls apart from a per-device cache
+ *   of the compute-unit count; calls may come from several host threads.
+ *
+ * The affine format (page "metaltile-std src/mlx/quantized.rs", qmv kernel
+ * header, layouts comment of the int8 kernel; page "mlx PR 4682", transposed
+ * quantized_matmul):
+ *   w_packed : uint32 [N, K*bits/32]; row n is a little-endian bit stream,
+ *              code q[n,k] is the unsigned field at stream bits
+ *              [k*bits, (k+1)*bits) (4-bit: 8 codes per word, low nibble
+ *              first; 8-bit: byte j of a word is code 4*word+j).
+ *   scales, biases : [N, K/group_size] in `dtype`.
+ *   x        : [M, K] in `dtype`.     out : [M, N] in `dtype`.
+ *   out[m,n] = sum_g ( scales[n,g] * sum_{k in g} q[n,k] * x[m,k]
+ *                    + biases[n,g] * sum_{k in g} x[m,k] )
+ *            = sum_k x[m,k] * (scales[n,k/gs] * q[n,k] + biases[n,k/gs]).
+ * Supported: bits in {2, 4, 8}; group_size in {32, 64, 128};
+ * K % group_size == 0.
+ */
+#ifndef QMX_H
+#define QMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMX_API_VERSION 1
+
+typedef enum qmx_dtype {
+    QMX_F32 = 0,   /* IEEE binary32 */
+    QMX_F16 = 1,   /* IEEE binary16 */
+    QMX_BF16 = 2   /* bfloat16 (upper half of a binary32) */
+} qmx_dtype;
+
+typedef enum qmx_status {
+    QMX_OK = 0,
+    QMX_ERR_NULL = -1,       /* a required pointer is NULL                        */
+    QMX_ERR_SHAPE = -2,      /* negative size, or a size the route cannot take     */
+    QMX_ERR_BITS = -3,       /* bits not in {2, 4, 8}                              */
+    QMX_ERR_GROUP = -4,      /* group_size not in {32, 64, 128} or K % gs != 0     */
+    QMX_ERR_DTYPE = -5,      /* unknown dtype, or a dtype the route does not take  */
+    QMX_ERR_ALIGN = -6,      /* a pointer lacks the alignment the route needs      */
+    QMX_ERR_WORKSPACE = -7,  /* split-K workspace NULL or too small                */
+    QMX_ERR_SPLITS = -8,     /* split count out of range for this K                */
+    QMX_ERR_LAUNCH = -9,     /* the HIP runtime rejected a launch                  */
+    QMX_ERR_DEVICE = -10     /* no usable HIP device                               */
+} qmx_status;
+
+typedef enum qmx_route {
+    QMX_ROUTE_QMV = 0,          /* qmx_qmv                      */
+    QMX_ROUTE_QMM_T = 1,        /* qmx_qmm_t (unsplit)          */
+    QMX_ROUTE_QMM_T_SPLITK = 2  /* qmx_qmm_t_splitk + accumulate */
+} qmx_route;
+
+/* Largest split count qmx_qmm_t_splitk accepts. */
+#define QMX_MAX_SPLITS 16
+
+/* qmx_qmv -- affine quantized matvec for small M (built for M = 1..7).
+ * Computes the affine definition above with float32 accumulation on the
+ * vector ALUs: weight codes are streamed once with 16-byte loads, the sum
+ * of x is formed once per group (bias hoist), lanes are reduced with a
+ * fixed-order cross-lane tree (page "metaltile-std src/mlx/quantized.rs",
+ * qmv kernel: bias hoist, x reuse across rows, simd_sum and lane-0 store).
+ * dtype: QMX_F32, QMX_F16 or QMX_BF16 for x, scales, biases and out.
+ * Any M >= 0 is accepted (rows of x are processed in tiles of up to 4).
+ * Extra requirements: (K*bits) % 128 == 0 (rows of w_packed are whole
+ * 16-byte chunks), w_packed 16-byte aligned, x aligned to its element size.
+ */
+int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases,
+            const void* x, void* out, int M, int N, int K, int bits, int group_size,
+            int dtype, void* stream);
+
+/* qmx_qmm_t -- affine quantized x * W^T for M >= 8 on the matrix cores
+ * (page "mlx PR 4682": staged transposed qmm with register prefetch, a
+ * double-buffered threadgroup-memory stage and one barrier per K step).
+ * Packed codes, x, scales and biases of the next K block are prefetched
+ * into registers while the matrix cores consume the current LDS buffer;
+ * the codes are expanded to exact 16-bit integers right before bf16/f16
+ * MFMA, and scale and bias are applied per group in float32, so the only
+ * rounding besides float32 accumulation is the final one.
+ * dtype: QMX_F16 or QMX_BF16 only (QMX_ERR_DTYPE for QMX_F32).
+ * Extra requirements: K % 128 == 0; w_packed, x 16-byte aligned.
+ */
+int qmx_qmm_t(const uint32_t* w_packed, const void* scales, const void* biases,
+              const void* x, void* out, int M, int N, int K, int bits, int group_size,
+              int dtype, void* stream);
+
+/* qmx_qmm_t_splitk -- qmx_qmm_t with K split into `splits` partitions
+ * (page "mlx PR 4682": split-K kernel writing float32 partials that a
+ * separate accumulate kernel sums, rounding once).  Partition p covers the
+ * 128-column K blocks [floor(p*nkb/splits), floor((p+1)*nkb/splits)) with
+ * nkb = K/128; each partition must hold at least two blocks (256 columns),
+ * so 2 <= splits <= min(QMX_MAX_SPLITS, K/256).  The first kernel writes
+ * workspace[p][m][n] (float32); the second sums p = 0..splits-1 in that
+ * order and rounds once to `dtype`.  workspace: device memory of at least
+ * qmx_splitk_workspace_bytes(M, N, splits) bytes, 16-byte aligned, owned by
+ * the caller, overwritten by the call (its contents on entry do not
+ * matter); calls that share one workspace must be ordered on one stream.
+ * Other requirements as qmx_qmm_t.
+ */
+int qmx_qmm_t_splitk(const uint32_t* w_packed, const void* scales, const void* biases,
+                     const void* x, void* out, int M, int N, int K, int bits, int group_size,
+                     int dtype, int splits, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Bytes of float32 partials qmx_qmm_t_splitk needs: splits * M * N * 4
+ * (0 for negative arguments). */
+size_t qmx_splitk_workspace_bytes(int M, int N, int splits);
+
+/* qmx_matvec_q8_0 -- Q8_0 block matvec, M = 1 (page "hanzo-kernel
+ * src/quant.rs": Q8_0 matvec and its packed layout).
+ * w_blocks: uint32 [N, K/32*9]; each 32-weight block is 9 words, the f16
+ * scale d in the low 16 bits of word 0 and 32 signed int8 quants in words
+ * 1..8 (quant i at byte i%4 of word 1+i/4).  x: float32 [K]; out: float32
+ * [N];  out[n] = sum_blocks d * sum_i q_i * x[32*block+i].
+ * Requirements: K % 32 == 0; w_blocks and x 16-byte aligned.
+ */
+int qmx_matvec_q8_0(const uint32_t* w_blocks, const float* x, float* out, int N, int K,
+                    void* stream);
+
+/* qmx_matvec_q4_k -- Q4_K super-block matvec, M = 1 (page "hanzo-kernel
+ * src/quant.rs": Q4_K block comment, scale/min unpack and kernel).
+ * w_blocks: uint32 [N, K/256*36]; each 144-byte super-block holds f16 d
+ * (bytes 0-1), f16 dmin (bytes 2-3), 12 bytes of packed 6-bit scales and
+ * mins (bytes 4-15) and 128 bytes of 4-bit quants (bytes 16-143).  Quant
+ * byte 32g+i gives element 64g+i (low nibble, sub-block 2g) and element
+ * 64g+32+i (high nibble, sub-block 2g+1); the weight of code q in sub-block
+ * j is d*sc_j*q - dmin*m_j.  x: float32 [K]; out: float32 [N].
+ * Requirements: K % 256 == 0; w_blocks and x 16-byte aligned.
+ */
+int qmx_matvec_q4_k(const uint32_t* w_blocks, const float* x, float* out, int N, int K,
+                    void* stream);
+
+/* qmx_plan -- the dispatch policy as a pure host function (page "mlx PR
+ * 4682", dispatch table and split rule; page "metaltile-std
+ * src/mlx/quantized.rs", M-based kernel selector).  Writes the route
+ * (qmx_route) and split count (1 when unsplit) that qmx_qmm would use for
+ * this problem on a device with `num_cus` compute units (num_cus <= 0:
+ * 256).  Performs no HIP call.  Returns QMX_OK or a validation status.
+ * route/splits: host pointers.
+ */
+int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus,
+             int* route, int* splits);
+
+/* Workspace bytes qmx_qmm needs for this problem (0 unless the plan picks
+ * split-K) on the current device.  Host function; may query the device's
+ * compute-unit count once. */
+size_t qmx_qmm_workspace_bytes(int M, int N, int K, int bits, int group_size, int dtype);
+
+/* qmx_qmm -- the policy-dispatched entry: runs qmx_qmv, qmx_qmm_t or
+ * qmx_qmm_t_splitk as qmx_plan decides for the current device.  workspace
+ * may be NULL when qmx_qmm_workspace_bytes() is 0; otherwise it must be at
+ * least that large (QMX_ERR_WORKSPACE if not). */
+int qmx_qmm(const uint32_t* w_packed, const void* scales, const void* biases,
+            const void* x, void* out, int M, int N, int K, int bits, int group_size,
+            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* qmx_strerror(int status);
+
+/* QMX_API_VERSION of the built library. */
+int qmx_api_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMX_H */

@@ -1,0 +1,12 @@
+// qmm_b2.hip -- 2-bit instances of the staged qmm_t kernel (kept apart so the
+// three code widths compile in parallel).
+#include "qmm_impl.h"
+
+namespace qmx {
+
+hipError_t qmm_launch_b2(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                         float* ws, int M, int N, int K, int gs, int dt, int splits, hipStream_t st) {
+    return qmm_launch_bits<2>(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+}
+
+}  // namespace qmx

@@ -1,0 +1,233 @@
+// qmx_api.cpp -- the C ABI declared in include/qmx.h: host-side validation,
+// the dispatch policy and the kernel launches.  Every check runs before any
+// HIP call, so argument errors never reach the device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "qmx.h"
+#include "qmx_internal.h"
+
+namespace {
+
+using qmx::QMM_BN;
+using qmx::QMM_KB;
+
+// Largest split count the dispatch policy picks by itself.
+constexpr int kPolicyMaxSplits = 4;
+// Default compute-unit count for planning without a device (MI355X).
+constexpr int kDefaultCUs = 256;
+
+bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t elem_bytes(int dt) { return dt == QMX_F32 ? 4 : 2; }
+
+// Checks shared by every affine route.
+int check_affine_common(int M, int N, int K, int bits, int gs, int dtype) {
+    if (dtype != QMX_F32 && dtype != QMX_F16 && dtype != QMX_BF16) return QMX_ERR_DTYPE;
+    if (bits != 2 && bits != 4 && bits != 8) return QMX_ERR_BITS;
+    if (gs != 32 && gs != 64 && gs != 128) return QMX_ERR_GROUP;
+    if (M < 0 || N < 0 || K < 0) return QMX_ERR_SHAPE;
+    if (K % gs != 0) return QMX_ERR_GROUP;
+    return QMX_OK;
+}
+
+int check_affine_ptrs(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int K,
+                      int dtype, uintptr_t w_align, uintptr_t x_align) {
+    if (!out) return QMX_ERR_NULL;
+    if (K > 0 && (!w || !s || !b || !x)) return QMX_ERR_NULL;
+    const uintptr_t e = elem_bytes(dtype);
+    if (!is_aligned(out, e)) return QMX_ERR_ALIGN;
+    if (K > 0) {
+        if (!is_aligned(w, w_align) || !is_aligned(x, x_align)) return QMX_ERR_ALIGN;
+        if (!is_aligned(s, e) || !is_aligned(b, e)) return QMX_ERR_ALIGN;
+    }
+    return QMX_OK;
+}
+
+int check_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int M, int N, int K,
+              int bits, int gs, int dtype) {
+    int rc = check_affine_common(M, N, K, bits, gs, dtype);
+    if (rc) return rc;
+    if (((long long)K * bits) % 128 != 0) return QMX_ERR_SHAPE;
+    if (M > 0 && (M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M) > 65535) return QMX_ERR_SHAPE;
+    if (M == 0 || N == 0) return QMX_OK;
+    return check_affine_ptrs(w, s, b, x, out, K, dtype, 16, 16);
+}
+
+int check_qmm(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int M, int N, int K,
+              int bits, int gs, int dtype, int splits) {
+    int rc = check_affine_common(M, N, K, bits, gs, dtype);
+    if (rc) return rc;
+    if (dtype == QMX_F32) return QMX_ERR_DTYPE;
+    if (K % QMM_KB != 0) return QMX_ERR_SHAPE;
+    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * (M > 0 ? qmx::qmm_mtiles_for(M) : 0);
+    if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
+    if (M == 0 || N == 0) return QMX_OK;
+    return check_affine_ptrs(w, s, b, x, out, K, dtype, 16, 16);
+}
+
+int max_splits_for(int K) {
+    const int by_k = K / (2 * QMM_KB);   // every partition holds at least 256 columns
+    return by_k < QMX_MAX_SPLITS ? by_k : QMX_MAX_SPLITS;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QMX_OK : QMX_ERR_LAUNCH; }
+
+// Compute units of the current device, cached per device id.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return -1;
+    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int* route, int* splits) {
+    int rc = check_affine_common(M, N, K, bits, gs, dtype);
+    if (rc) return rc;
+    if (num_cus <= 0) num_cus = kDefaultCUs;
+    // float32, M < 8 and K that the staged kernel cannot block stay on qmv.
+    if (dtype == QMX_F32 || M < 8 || K % QMM_KB != 0) {
+        if (((long long)K * bits) % 128 != 0) return QMX_ERR_SHAPE;
+        *route = QMX_ROUTE_QMV;
+        *splits = 1;
+        return QMX_OK;
+    }
+    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
+    *route = QMX_ROUTE_QMM_T;
+    *splits = 1;
+    if (K < 4 * QMM_KB || tiles >= num_cus || tiles == 0) return QMX_OK;
+    long long s = (num_cus + tiles - 1) / tiles;
+    const int cap = max_splits_for(K) < kPolicyMaxSplits ? max_splits_for(K) : kPolicyMaxSplits;
+    if (s > cap) s = cap;
+    if (s >= 2) {
+        *route = QMX_ROUTE_QMM_T_SPLITK;
+        *splits = (int)s;
+    }
+    return QMX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmx_api_version(void) { return QMX_API_VERSION; }
+
+const char* qmx_strerror(int status) {
+    switch (status) {
+        case QMX_OK: return "success";
+        case QMX_ERR_NULL: return "a required pointer is NULL";
+        case QMX_ERR_SHAPE: return "unsupported or negative problem size for this route";
+        case QMX_ERR_BITS: return "bits must be 2, 4 or 8";
+        case QMX_ERR_GROUP: return "group_size must be 32, 64 or 128 and divide K";
+        case QMX_ERR_DTYPE: return "unsupported dtype for this route";
+        case QMX_ERR_ALIGN: return "a pointer is not aligned as the route requires";
+        case QMX_ERR_WORKSPACE: return "split-K workspace is NULL, misaligned or too small";
+        case QMX_ERR_SPLITS: return "split count out of range for this K";
+        case QMX_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case QMX_ERR_DEVICE: return "no usable HIP device";
+        default: return "unknown status";
+    }
+}
+
+int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
+            int M, int N, int K, int bits, int group_size, int dtype, void* stream) {
+    const int rc = check_qmv(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype);
+    if (rc || M == 0 || N == 0) return rc;
+    return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int qmx_qmm_t(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
+              int M, int N, int K, int bits, int group_size, int dtype, void* stream) {
+    const int rc = check_qmm(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, 1);
+    if (rc || M == 0 || N == 0) return rc;
+    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, M, N, K, bits,
+                                           group_size, dtype, 1, static_cast<hipStream_t>(stream)));
+}
+
+size_t qmx_splitk_workspace_bytes(int M, int N, int splits) {
+    if (M < 0 || N < 0 || splits < 0) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int qmx_qmm_t_splitk(const uint32_t* w_packed, const void* scales, const void* biases, const void* x,
+                     void* out, int M, int N, int K, int bits, int group_size, int dtype, int splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (splits < 2 || splits > QMX_MAX_SPLITS) return QMX_ERR_SPLITS;
+    int rc = check_qmm(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, splits);
+    if (rc) return rc;
+    if (splits > max_splits_for(K)) return QMX_ERR_SPLITS;
+    if (M == 0 || N == 0) return QMX_OK;
+    if (!workspace || !is_aligned(workspace, 16) ||
+        workspace_bytes < qmx_splitk_workspace_bytes(M, N, splits))
+        return QMX_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, M, N, K, bits, group_size,
+                                         dtype, splits, st));
+    if (rc) return rc;
+    return launch_status(qmx::launch_splitk_accum(ws, out, splits, (size_t)M * N, dtype, st));
+}
+
+int qmx_matvec_q8_0(const uint32_t* w_blocks, const float* x, float* out, int N, int K, void* stream) {
+    if (N < 0 || K < 0) return QMX_ERR_SHAPE;
+    if (K % 32 != 0) return QMX_ERR_GROUP;
+    if (N == 0) return QMX_OK;
+    if (!out || (K > 0 && (!w_blocks || !x))) return QMX_ERR_NULL;
+    if (!is_aligned(out, 4) || (K > 0 && (!is_aligned(w_blocks, 16) || !is_aligned(x, 16))))
+        return QMX_ERR_ALIGN;
+    return launch_status(qmx::launch_q8_0(w_blocks, x, out, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmx_matvec_q4_k(const uint32_t* w_blocks, const float* x, float* out, int N, int K, void* stream) {
+    if (N < 0 || K < 0) return QMX_ERR_SHAPE;
+    if (K % 256 != 0) return QMX_ERR_GROUP;
+    if (N == 0) return QMX_OK;
+    if (!out || (K > 0 && (!w_blocks || !x))) return QMX_ERR_NULL;
+    if (!is_aligned(out, 4) || (K > 0 && (!is_aligned(w_blocks, 16) || !is_aligned(x, 16))))
+        return QMX_ERR_ALIGN;
+    return launch_status(qmx::launch_q4_k(w_blocks, x, out, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus, int* route, int* splits) {
+    if (!route || !splits) return QMX_ERR_NULL;
+    return plan_impl(M, N, K, bits, group_size, dtype, num_cus, route, splits);
+}
+
+size_t qmx_qmm_workspace_bytes(int M, int N, int K, int bits, int group_size, int dtype) {
+    int route = 0, splits = 1;
+    if (plan_impl(M, N, K, bits, group_size, dtype, device_cus(), &route, &splits) != QMX_OK) return 0;
+    return route == QMX_ROUTE_QMM_T_SPLITK ? qmx_splitk_workspace_bytes(M, N, splits) : 0;
+}
+
+int qmx_qmm(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
+            int M, int N, int K, int bits, int group_size, int dtype, void* workspace, size_t workspace_bytes,
+            void* stream) {
+    int route = 0, splits = 1;
+    int rc = check_affine_common(M, N, K, bits, group_size, dtype);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return QMX_OK;
+    const int cus = device_cus();
+    if (cus <= 0) return QMX_ERR_DEVICE;
+    rc = plan_impl(M, N, K, bits, group_size, dtype, cus, &route, &splits);
+    if (rc) return rc;
+    if (route == QMX_ROUTE_QMV)
+        return qmx_qmv(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, stream);
+    if (route == QMX_ROUTE_QMM_T)
+        return qmx_qmm_t(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, stream);
+    return qmx_qmm_t_splitk(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, splits,
+                            workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// qmx_internal.h -- host-side launchers shared between the kernel sources and
+// the C ABI in qmx_api.cpp.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmx {
+
+// Rows of W per qmv wave, and rows of x per qmv wave tile.
+constexpr int QMV_ROWS = 4;
+int qmv_mt_for(int M);
+
+// qmm_t geometry: 4 waves of 2 x 16 columns, 128-column K blocks.
+constexpr int QMM_WAVES = 4;
+constexpr int QMM_NB = 2;
+constexpr int QMM_BN = QMM_WAVES * QMM_NB * 16;
+constexpr int QMM_KB = 128;
+constexpr int QMM_THREADS = QMM_WAVES * 64;
+// 16-row x fragments per tile chosen for M (1, 2, 3, 4, 6 or 8) and the tile count.
+int qmm_mt_for(int M);
+int qmm_mtiles_for(int M);
+
+hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                      int M, int N, int K, int bits, int gs, int dt, hipStream_t st);
+
+// splits == 1: writes `out` in dtype dt.  splits > 1: writes float32
+// partials ws[p][M][N] (the accumulate kernel is launched separately).
+hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                        float* ws, int M, int N, int K, int bits, int gs, int dt, int splits,
+                        hipStream_t st);
+
+hipError_t launch_splitk_accum(const float* ws, void* out, int splits, size_t MN, int dt,
+                               hipStream_t st);
+
+hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st);
+hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st);
+
+}  // namespace qmx

@@ -21,9 +21,11 @@ Q4_K block comments):
   ``d``, bytes 2-3 f16 ``dmin``, bytes 4-15 the 12 packed 6-bit scale/min
   bytes, bytes 16-143 the 128 bytes of 4-bit quants.
 
-Random draws use numpy ``PCG64``; values are drawn in f32 and rounded
-round-to-nearest-even to the storage dtype.  Draw order: codes, scales, bias
-jitter, x.
+Random draws use numpy ``PCG64``; integer codes and quant bytes are random
+bytes (b-bit codes are their low b bits, so every code value is equally
+likely; Q8_0 bytes equal to -128 are drawn again); values are drawn in f32
+and rounded round-to-nearest-even to the storage dtype.  Draw order: codes,
+scales, bias jitter, x.
 """
 from __future__ import annotations
 
@@ -85,9 +87,22 @@ def pack_codes(codes, bits: int) -> np.ndarray:
     if (k * bits) % 32:
         raise ValueError("K*bits must be a multiple of 32")
     per = 32 // bits
-    c = codes.astype(np.uint32).reshape(n, k // per, per)
-    shifts = (np.arange(per, dtype=np.uint32) * bits)
-    return np.bitwise_or.reduce(c << shifts, axis=2).astype(np.uint32)
+    out = np.zeros((n, k // per), dtype=np.uint32)
+    for j in range(per):
+        out |= codes[:, j::per].astype(np.uint32) << np.uint32(bits * j)
+    return out
+
+
+def random_codes(rng, shape, bits: int) -> np.ndarray:
+    """Codes uniform on 0..2^bits-1: the low ``bits`` bits of random bytes."""
+    n = int(np.prod(shape))
+    raw = np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape)
+    return raw & np.uint8((1 << bits) - 1)
+
+
+def random_bytes(rng, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape).copy()
 
 
 def bytes_to_words(b) -> np.ndarray:
@@ -106,7 +121,7 @@ def affine_case(M, N, K, bits, gs, dtype, seed, bias="jitter", x_dist="normal"):
         raise ValueError("K must be a multiple of group_size")
     rng = np.random.Generator(np.random.PCG64(seed))
     G = K // gs
-    codes = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    codes = random_codes(rng, (N, K), bits)
     s32 = rng.uniform(0.002, 0.02, size=(N, G)).astype(np.float32)
     half = np.float32(1 << (bits - 1))
     if bias == "jitter":
@@ -139,7 +154,11 @@ def q8_0_case(N, K, seed):
         raise ValueError("K must be a multiple of 32")
     rng = np.random.Generator(np.random.PCG64(seed))
     nb = K // 32
-    q = rng.integers(-127, 128, size=(N, K), dtype=np.int16).astype(np.int8)
+    q = random_bytes(rng, (N, K)).view(np.int8)
+    bad = q == -128                      # redraw -128 so quants are uniform on -127..127
+    while bad.any():
+        q[bad] = random_bytes(rng, (int(bad.sum()),)).view(np.int8)
+        bad = q == -128
     d = rng.uniform(0.001, 0.01, size=(N, nb)).astype(np.float32).astype(np.float16)
     x = rng.standard_normal(K).astype(np.float32)
     return {"N": N, "K": K, "q": q, "d": d, "x": x,
@@ -166,8 +185,8 @@ def q4_k_case(N, K, seed):
         raise ValueError("K must be a multiple of 256")
     rng = np.random.Generator(np.random.PCG64(seed))
     nb = K // 256
-    qs = rng.integers(0, 256, size=(N, nb, 128), dtype=np.uint16).astype(np.uint8)
-    sc = rng.integers(0, 256, size=(N, nb, 12), dtype=np.uint16).astype(np.uint8)
+    qs = random_bytes(rng, (N, nb, 128))
+    sc = random_bytes(rng, (N, nb, 12))
     d = rng.uniform(0.002, 0.052, size=(N, nb)).astype(np.float32).astype(np.float16)
     dmin = rng.uniform(0.0, 0.025, size=(N, nb)).astype(np.float32).astype(np.float16)
     x = rng.standard_normal(K).astype(np.float32)

@@ -1,0 +1,168 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+rejects bad arguments before any HIP call, and the dispatch policy table.
+
+No compute call is made here (no GPU in this tier); argument errors return
+before the library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmx.h")
+
+import matmul_affine_qmv_amd as qmx  # noqa: E402
+
+if not os.path.exists(qmx.LIB_PATH):
+    pytest.skip("libqmx.so not built", allow_module_level=True)
+
+OK, ENULL, ESHAPE, EBITS, EGROUP, EDTYPE, EALIGN, EWS, ESPLITS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"qmx_qmv", "qmx_qmm_t", "qmx_qmm_t_splitk", "qmx_matvec_q8_0", "qmx_matvec_q4_k",
+            "qmx_qmm", "qmx_plan"} <= set(names)
+    raw = ctypes.CDLL(qmx.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(qmx._EXPORTS), "binding and header disagree"
+
+
+def test_version_and_strerror():
+    assert qmx.api_version() == 1
+    for code in range(-10, 1):
+        assert qmx.strerror(code) and qmx.strerror(code) != "unknown status"
+    assert qmx.strerror(-99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x10002)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+# The calls below pass placeholder pointers that must never reach a kernel.  They
+# are meant for the CPU tier; on a machine with a GPU a validation slip would
+# launch a kernel on them, so there they are skipped.
+fake_ptr_test = pytest.mark.skipif(_gpu_visible(), reason="placeholder pointers: CPU-only checks")
+
+
+def qmv(w=FAKE, s=FAKE, b=FAKE, x=FAKE, o=FAKE, M=1, N=64, K=4096, bits=4, gs=64, dt=BF16):
+    return qmx.lib().qmx_qmv(w, s, b, x, o, M, N, K, bits, gs, dt, None)
+
+
+def qmm_t(w=FAKE, s=FAKE, b=FAKE, x=FAKE, o=FAKE, M=16, N=64, K=4096, bits=4, gs=64, dt=BF16):
+    return qmx.lib().qmx_qmm_t(w, s, b, x, o, M, N, K, bits, gs, dt, None)
+
+
+def splitk(splits=2, ws=FAKE, wsb=1 << 30, M=16, N=64, K=4096, bits=4, gs=64, dt=BF16, x=FAKE, w=FAKE):
+    return qmx.lib().qmx_qmm_t_splitk(w, FAKE, FAKE, x, FAKE, M, N, K, bits, gs, dt, splits, ws, wsb, None)
+
+
+@fake_ptr_test
+def test_qmv_validation():
+    assert qmv(bits=3) == EBITS
+    assert qmv(bits=16) == EBITS
+    assert qmv(gs=16) == EGROUP
+    assert qmv(K=4000) == EGROUP           # not a multiple of 64
+    assert qmv(dt=7) == EDTYPE
+    assert qmv(M=-1) == ESHAPE
+    assert qmv(N=-4) == ESHAPE
+    assert qmv(K=96, gs=32, bits=2) == ESHAPE   # 192 bits per row is not whole 16-byte chunks
+    assert qmv(o=None) == ENULL
+    assert qmv(w=None) == ENULL
+    assert qmv(x=None) == ENULL
+    assert qmv(w=ODD) == EALIGN
+    assert qmv(x=ODD) == EALIGN
+    # empty problems succeed without touching the device or the pointers
+    assert qmv(M=0, w=None, x=None, o=None) == OK
+    assert qmv(N=0, w=None, x=None, o=None) == OK
+
+
+@fake_ptr_test
+def test_qmm_t_validation():
+    assert qmm_t(dt=F32) == EDTYPE
+    assert qmm_t(K=4032) == ESHAPE          # K % 128 != 0 (but K % 64 == 0)
+    assert qmm_t(bits=5) == EBITS
+    assert qmm_t(gs=256) == EGROUP
+    assert qmm_t(s=None) == ENULL
+    assert qmm_t(x=ODD) == EALIGN
+    assert qmm_t(M=0, w=None) == OK
+
+
+@fake_ptr_test
+def test_splitk_validation():
+    assert splitk(splits=1) == ESPLITS
+    assert splitk(splits=17) == ESPLITS
+    assert splitk(splits=3, K=512) == ESPLITS      # 512/3 < 256 columns per partition
+    assert splitk(splits=2, K=512, ws=None) == EWS
+    assert splitk(splits=4, wsb=4 * 16 * 64 * 4 - 4) == EWS
+    assert splitk(splits=4, ws=ctypes.c_void_p(0x10004)) == EWS
+    assert qmx.splitk_workspace_bytes(85, 2048, 4) == 4 * 85 * 2048 * 4
+    assert qmx.splitk_workspace_bytes(-1, 2, 2) == 0
+
+
+@fake_ptr_test
+def test_block_validation():
+    L = qmx.lib()
+    assert L.qmx_matvec_q8_0(FAKE, FAKE, FAKE, 16, 48, None) == EGROUP
+    assert L.qmx_matvec_q8_0(FAKE, FAKE, None, 16, 64, None) == ENULL
+    assert L.qmx_matvec_q8_0(ODD, FAKE, FAKE, 16, 64, None) == EALIGN
+    assert L.qmx_matvec_q8_0(FAKE, FAKE, FAKE, -1, 64, None) == ESHAPE
+    assert L.qmx_matvec_q8_0(None, None, None, 0, 64, None) == OK
+    assert L.qmx_matvec_q4_k(FAKE, FAKE, FAKE, 16, 128, None) == EGROUP
+    assert L.qmx_matvec_q4_k(FAKE, ODD, FAKE, 16, 256, None) == EALIGN
+    assert L.qmx_matvec_q4_k(None, None, None, 0, 256, None) == OK
+
+
+@pytest.mark.parametrize("M,N,K,dtype,route,splits", [
+    (1, 4096, 4096, BF16, "qmv", 1),
+    (7, 4096, 4096, BF16, "qmv", 1),
+    (16, 4096, 4096, F32, "qmv", 1),                 # float32 never takes the matrix cores
+    (16, 4096, 4096, BF16, "qmm_t_splitk", 4),       # 32 tiles on 256 CUs
+    (16, 4096, 256, BF16, "qmm_t", 1),               # K < 512 stays unsplit
+    (22, 2048, 2048, BF16, "qmm_t_splitk", 4),
+    (85, 2048, 10752, BF16, "qmm_t_splitk", 4),
+    (33, 4096, 14336, BF16, "qmm_t_splitk", 4),
+    (56, 5120, 17408, BF16, "qmm_t_splitk", 4),
+    (512, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 4 M tiles x 32 N tiles = 128 tiles
+    (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
+    (8, 4096, 4096, F16, "qmm_t_splitk", 4),
+    (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
+])
+def test_plan_table(M, N, K, dtype, route, splits):
+    assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)
+
+
+def test_plan_respects_split_limits():
+    for K in (512, 768, 1024, 2048, 14336):
+        for N in (128, 1024, 4096):
+            route, s = qmx.plan(16, N, K, 4, 64, BF16, 256)
+            if route == "qmm_t_splitk":
+                assert 2 <= s <= 4 and K // s >= 256
+    with pytest.raises(qmx.QmxError):
+        qmx.plan(16, 4096, 96, 2, 32, F32, 256)      # qmv route cannot take 192-bit rows
+    with pytest.raises(qmx.QmxError):
+        qmx.plan(1, 4096, 4096, 3, 64, BF16, 256)
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, dtype=torch.bfloat16)
+    w = torch.zeros(8, 8, dtype=torch.int32)
+    s = torch.zeros(8, 1, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qmx.qmv(w, s, s, x, bits=4, group_size=64)

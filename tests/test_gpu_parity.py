@@ -1,0 +1,276 @@
+"""HIP path against the float64 oracle, through the C ABI (needs a gfx950 GPU).
+
+Small cases cover several tiles and ragged tails and are checked on every
+output; the full workload sizes are checked on sampled columns (all rows)
+that the oracle computes one by one.  Every case prints its name before it
+touches the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import qmx_inputs as qi
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import matmul_affine_qmv_amd as qmx  # noqa: E402
+
+DEV = "cuda:0"
+TORCH_DT = {qi.F32: torch.float32, qi.F16: torch.float16, qi.BF16: torch.bfloat16}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(case):
+    dt = case["dtype"]
+    return (qmx.words_tensor(case["w"], DEV), qmx.storage_tensor(case["scales"], dt, DEV),
+            qmx.storage_tensor(case["biases"], dt, DEV), qmx.storage_tensor(case["x"], dt, DEV))
+
+
+def out64(t, dt):
+    return qi.storage_to_f64(qmx.tensor_bits(t), dt)
+
+
+def sample_cols(N, count, seed):
+    if N <= count:
+        return np.arange(N, dtype=np.int32)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    edge = np.r_[0:16, N - 16:N]
+    rest = rng.choice(np.arange(16, N - 16), size=count - edge.size, replace=False)
+    return np.unique(np.r_[edge, rest]).astype(np.int32)
+
+
+def run(route, w, s, b, x, bits, gs, splits=None, workspace=None):
+    if route == "qmv":
+        return qmx.qmv(w, s, b, x, bits=bits, group_size=gs)
+    if route == "qmm_t":
+        return qmx.qmm_t(w, s, b, x, bits=bits, group_size=gs)
+    if route == "splitk":
+        return qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=splits, workspace=workspace)
+    return qmx.qmm(w, s, b, x, bits=bits, group_size=gs)
+
+
+def check_affine(orc, route, M, N, K, bits, gs, dt, seed, splits=None, cols=None, bias="jitter",
+                 reruns=0):
+    say(route, f"M={M} N={N} K={K} bits={bits} gs={gs} dt={qi.DTYPE_NAMES[dt]} splits={splits} seed={seed}")
+    c = qi.affine_case(M, N, K, bits, gs, dt, seed=seed, bias=bias)
+    w, s, b, x = to_dev(c)
+    y = run(route, w, s, b, x, bits, gs, splits)
+    torch.cuda.synchronize()
+    got = out64(y, dt)
+    ref = orc.affine_case(c, cols=cols)
+    if cols is not None:
+        got = got[:, cols]
+    m = assert_close(got, ref, dt, orc, what=f"{route} {M}x{N}x{K} b{bits} gs{gs} dt{dt} S{splits}")
+    for _ in range(reruns):
+        y2 = run(route, w, s, b, x, bits, gs, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16) if y.dtype != torch.float32 else y.view(torch.int32),
+                           y2.view(torch.int16) if y2.dtype != torch.float32 else y2.view(torch.int32)), \
+            "rerun not bit-identical"
+    return m
+
+
+# ---------------------------------------------------------------- qmv
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [qi.F32, qi.F16, qi.BF16])
+def test_qmv_small_all_formats(orc, bits, gs, dt):
+    # ragged N (not a multiple of 4 rows), K spanning several 64-lane chunk rounds plus a tail
+    K = 2560 if bits != 2 else 2560
+    check_affine(orc, "qmv", 1, 67, K, bits, gs, dt, seed=1000 + bits * 100 + gs + dt)
+
+
+@pytest.mark.parametrize("M", [2, 3, 5, 7])
+def test_qmv_small_m(orc, M):
+    check_affine(orc, "qmv", M, 45, 1024, 4, 64, qi.BF16, seed=1100 + M)
+    check_affine(orc, "qmv", M, 18, 512, 8, 32, qi.F32, seed=1150 + M)
+
+
+def test_qmv_config1_full(orc):
+    # M=1, N=K=4096, 4-bit gs64, float32 everywhere (all outputs checked, reruns bit-identical)
+    check_affine(orc, "qmv", 1, 4096, 4096, 4, 64, qi.F32, seed=qi.seed_for(1, 0), reruns=2)
+
+
+@pytest.mark.parametrize("NK", [(5120, 5120), (14336, 5120), (5120, 14336), (27648, 5120)])
+@pytest.mark.parametrize("dt", [qi.F32, qi.F16, qi.BF16])
+def test_qmv_config2_full(orc, NK, dt):
+    N, K = NK
+    check_affine(orc, "qmv", 1, N, K, 4, 64, dt, seed=qi.seed_for(2, N // 1024 + K // 1024 + dt))
+
+
+# ---------------------------------------------------------------- qmm_t and split-K
+@pytest.mark.parametrize("M", [8, 9, 16, 22, 33, 56, 85, 128, 129, 200])
+def test_qmm_t_small_m_tails(orc, M):
+    check_affine(orc, "qmm_t", M, 200, 512, 4, 64, qi.BF16, seed=1200 + M)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
+def test_qmm_t_small_all_formats(orc, bits, gs, dt):
+    check_affine(orc, "qmm_t", 37, 160, 768, bits, gs, dt, seed=1300 + bits * 100 + gs + dt)
+    check_affine(orc, "splitk", 37, 160, 768, bits, gs, dt, seed=1300 + bits * 100 + gs + dt, splits=3)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 4, 5, 8])
+def test_splitk_every_count(orc, splits):
+    check_affine(orc, "splitk", 22, 384, 2048, 4, 64, qi.BF16, seed=1400 + splits, splits=splits, reruns=2)
+
+
+CONFIG3 = [(2048, 2048, 22), (4096, 4096, 16), (256, 4096, 16), (10752, 2048, 85), (14336, 4096, 33),
+           (17408, 5120, 56), (4096, 4096, 512)]
+
+
+@pytest.mark.parametrize("KNM", CONFIG3)
+def test_qmm_config3_policy(orc, KNM):
+    K, N, M = KNM
+    cols = sample_cols(N, 384, seed=K + N + M)
+    check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=qi.seed_for(3, M), cols=cols, reruns=1)
+
+
+@pytest.mark.parametrize("KNM", [(2048, 2048, 22), (10752, 2048, 85), (17408, 5120, 56)])
+@pytest.mark.parametrize("route", ["qmm_t", "s2", "s3", "s4"])
+def test_qmm_config3_every_route(orc, KNM, route):
+    K, N, M = KNM
+    cols = sample_cols(N, 256, seed=K + N + M + 1)
+    if route == "qmm_t":
+        check_affine(orc, "qmm_t", M, N, K, 4, 64, qi.BF16, seed=qi.seed_for(3, M), cols=cols)
+    else:
+        check_affine(orc, "splitk", M, N, K, 4, 64, qi.BF16, seed=qi.seed_for(3, M), cols=cols,
+                     splits=int(route[1:]))
+
+
+def test_splitk_partials_match_partition_oracle(orc):
+    """workspace[p] is the float32 partial of partition p: its K blocks are
+    [floor(p*nkb/S), floor((p+1)*nkb/S)) of 128 columns."""
+    M, N, K, bits, gs, dt, S = 22, 256, 1664, 4, 64, qi.BF16, 3
+    say("splitk partials", M, N, K, S)
+    c = qi.affine_case(M, N, K, bits, gs, dt, seed=1500)
+    w, s, b, x = to_dev(c)
+    ws = torch.empty(S * M * N, dtype=torch.float32, device=DEV)
+    y = qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    nkb = K // 128
+    parts = ws.view(S, M, N).cpu().numpy().astype(np.float64)
+    for p in range(S):
+        kb0, kb1 = p * nkb // S, (p + 1) * nkb // S
+        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs,
+                                kb0 * 128 // gs, kb1 * 128 // gs)
+        assert_close(parts[p], ref, qi.F32, orc, what=f"partial {p}")
+    # the output is the rounded sum of the partials in ascending order
+    acc = parts[0].astype(np.float32)
+    for p in range(1, S):
+        acc = (acc + parts[p].astype(np.float32)).astype(np.float32)
+    want = orc.round(acc.astype(np.float64), dt)
+    assert np.array_equal(out64(y, dt), want)
+
+
+# ---------------------------------------------------------------- affine sweep (bits x gs x dtype x M)
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
+def test_config4_sweep(orc, bits, gs, dt):
+    N = K = 4096
+    for M in (1, 8, 33, 128, 257):
+        cols = sample_cols(N, 192, seed=bits * 1000 + gs + M)
+        check_affine(orc, "qmm", M, N, K, bits, gs, dt, seed=qi.seed_for(4, bits * 100 + gs + M + dt),
+                     cols=cols, bias="exact")
+
+
+# ---------------------------------------------------------------- Q8_0 / Q4_K
+def test_q8_0_config5(orc):
+    N, K = 14336, 5120
+    say("q8_0", N, K)
+    c = qi.q8_0_case(N, K, seed=qi.seed_for(5, 0))
+    wb = qmx.words_tensor(c["blocks"], DEV)
+    x = torch.from_numpy(c["x"]).to(DEV)
+    y = qmx.matvec_q8_0(wb, x)
+    y2 = qmx.matvec_q8_0(wb, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert_close(y.cpu().numpy().astype(np.float64), orc.q8_0(c["blocks"], c["x"], N, K), qi.F32, orc, "q8_0")
+
+
+def test_q4_k_config5(orc):
+    N, K = 14336, 5120
+    say("q4_k", N, K)
+    c = qi.q4_k_case(N, K, seed=qi.seed_for(5, 1))
+    wb = qmx.words_tensor(c["blocks"], DEV)
+    x = torch.from_numpy(c["x"]).to(DEV)
+    y = qmx.matvec_q4_k(wb, x)
+    y2 = qmx.matvec_q4_k(wb, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    assert_close(y.cpu().numpy().astype(np.float64), orc.q4_k(c["blocks"], c["x"], N, K), qi.F32, orc, "q4_k")
+
+
+@pytest.mark.parametrize("NK", [(1, 256), (7, 512), (33, 1280), (130, 4096)])
+def test_blocks_small_ragged(orc, NK):
+    N, K = NK
+    say("blocks", N, K)
+    c8 = qi.q8_0_case(N, K, seed=1600 + N)
+    y = qmx.matvec_q8_0(qmx.words_tensor(c8["blocks"], DEV), torch.from_numpy(c8["x"]).to(DEV))
+    assert_close(y.cpu().numpy().astype(np.float64), orc.q8_0(c8["blocks"], c8["x"], N, K), qi.F32, orc)
+    c4 = qi.q4_k_case(N, K, seed=1700 + N)
+    y = qmx.matvec_q4_k(qmx.words_tensor(c4["blocks"], DEV), torch.from_numpy(c4["x"]).to(DEV))
+    assert_close(y.cpu().numpy().astype(np.float64), orc.q4_k(c4["blocks"], c4["x"], N, K), qi.F32, orc)
+
+
+# ---------------------------------------------------------------- edge cases
+def test_empty_and_zero_k(orc):
+    say("edge: empty and K=0")
+    for route in ("qmv", "qmm_t", "qmm"):
+        # M = 0 and N = 0: nothing launched, nothing written
+        for M, N in ((0, 64), (16, 0)):
+            x = torch.zeros(M, 256, dtype=torch.bfloat16, device=DEV)
+            w = torch.zeros(N, 32, dtype=torch.int32, device=DEV)
+            s = torch.zeros(N, 4, dtype=torch.bfloat16, device=DEV)
+            y = run(route, w, s, s, x, 4, 64)
+            assert y.shape == (M, N)
+        # K = 0: the sum over no terms is zero
+        M = 1 if route == "qmv" else 16
+        x = torch.zeros(M, 0, dtype=torch.bfloat16, device=DEV)
+        w = torch.zeros(40, 0, dtype=torch.int32, device=DEV)
+        s = torch.zeros(40, 0, dtype=torch.bfloat16, device=DEV)
+        out = torch.full((M, 40), 7.0, dtype=torch.bfloat16, device=DEV)
+        y = run(route, w, s, s, x, 4, 64) if route != "qmm" else qmx.qmm(w, s, s, x, out, bits=4, group_size=64)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(y.float()).item() == 0
+
+
+def test_degenerate_values(orc):
+    """All-zero codes give sum_g bias*sum(x); scale 1 / bias 0 with integer x gives the exact
+    integer product of the codes."""
+    say("edge: degenerate values")
+    M, N, K = 16, 128, 1024
+    c = qi.affine_case(M, N, K, 4, 64, qi.F32, seed=1800)
+    c["w"][:] = 0
+    xi = np.random.Generator(np.random.PCG64(1801)).integers(-3, 4, size=(1, K)).astype(np.float32)
+    c1 = dict(c, x=xi, M=1, scales=np.ones_like(c["scales"]), biases=np.zeros_like(c["biases"]),
+              w=qi.pack_codes(c["codes"], 4))
+    w, s, b, x = to_dev(c1)
+    y = qmx.qmv(w, s, b, x, bits=4, group_size=64)
+    want = xi.astype(np.int64) @ c["codes"].astype(np.int64).T
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want.astype(np.float64))
+    for dt in (qi.BF16, qi.F16):
+        cz = qi.affine_case(M, N, K, 4, 64, dt, seed=1802)
+        cz["w"][:] = 0
+        w, s, b, x = to_dev(cz)
+        y = qmx.qmm_t(w, s, b, x, bits=4, group_size=64)
+        assert_close(out64(y, dt), orc.affine_case(cz), dt, orc, "zero codes")
+
+
+def test_large_n_and_m(orc):
+    # widest configured row count on qmv and a large M on the matrix cores (sampled columns)
+    check_affine(orc, "qmv", 1, 27648, 5120, 4, 64, qi.BF16, seed=1900, cols=sample_cols(27648, 512, 1))
+    check_affine(orc, "qmm", 1024, 1024, 2048, 4, 64, qi.BF16, seed=1901, cols=sample_cols(1024, 128, 2))
