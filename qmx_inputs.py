@@ -204,3 +204,65 @@ def q4_k_blocks(d, dmin, scale_bytes, qs) -> np.ndarray:
     raw[:, :, 4:16] = scale_bytes
     raw[:, :, 16:144] = qs
     return bytes_to_words(raw).reshape(n, nb * 36)
+
+
+# ---------------------------------------------------------------- device-side draws (bench)
+def affine_case_torch(M, N, K, bits, gs, dtype, seed, device, bias="jitter"):
+    """The affine workload drawn directly on a torch device (seeded Philox).
+
+    Same distributions as ``affine_case``: packed words are random 32-bit
+    words, so every b-bit code is uniform; scales U(0.002, 0.02) and the bias
+    rule in f32, rounded to ``dtype``; x ~ N(0, 1).  Returns device tensors
+    ``w`` (int32 bits), ``scales``, ``biases``, ``x``.
+    """
+    import torch
+    dt = dtype_code(dtype)
+    tdt = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dt]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    G = K // gs
+    w = torch.randint(-(2 ** 31), 2 ** 31, (N, K * bits // 32), dtype=torch.int64, generator=g,
+                      device=device).to(torch.int32)
+    s32 = torch.rand((N, G), generator=g, device=device, dtype=torch.float32) * 0.018 + 0.002
+    half = float(1 << (bits - 1))
+    if bias == "jitter":
+        jit = torch.rand((N, G), generator=g, device=device, dtype=torch.float32) * 0.2 - 0.1
+        b32 = (-half * s32) * (1.0 + jit)
+    else:
+        b32 = -half * s32
+    x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+    return {"M": M, "N": N, "K": K, "bits": bits, "gs": gs, "dtype": dt, "seed": seed,
+            "w": w, "scales": s32.to(tdt), "biases": b32.to(tdt), "x": x.to(tdt)}
+
+
+def q8_0_case_torch(N, K, seed, device):
+    """Q8_0 blocks drawn on a device: quants U{-127..127}, f16 d U(0.001, 0.01), x ~ N(0,1)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nb = K // 32
+    q = torch.randint(-127, 128, (N, nb, 32), dtype=torch.int32, generator=g, device=device)
+    b = (q & 0xFF).reshape(N, nb, 8, 4)
+    words = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    d = (torch.rand((N, nb), generator=g, device=device) * 0.009 + 0.001).to(torch.float16)
+    d_word = d.view(torch.int16).to(torch.int32) & 0xFFFF
+    blocks = torch.cat([d_word.unsqueeze(-1), words], dim=-1).reshape(N, nb * 9).contiguous()
+    x = torch.randn(K, generator=g, device=device, dtype=torch.float32)
+    return {"N": N, "K": K, "blocks": blocks, "x": x, "seed": seed}
+
+
+def q4_k_case_torch(N, K, seed, device):
+    """Q4_K super-blocks drawn on a device: random scale/quant bytes, f16 d U[0.002, 0.052),
+    f16 dmin U[0, 0.025), x ~ N(0,1)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nb = K // 256
+    body = torch.randint(-(2 ** 31), 2 ** 31, (N, nb, 35), dtype=torch.int64, generator=g,
+                         device=device).to(torch.int32)
+    d = (torch.rand((N, nb), generator=g, device=device) * 0.05 + 0.002).to(torch.float16)
+    dmin = (torch.rand((N, nb), generator=g, device=device) * 0.025).to(torch.float16)
+    w0 = (d.view(torch.int16).to(torch.int32) & 0xFFFF) | (dmin.view(torch.int16).to(torch.int32) << 16)
+    blocks = torch.cat([w0.unsqueeze(-1), body], dim=-1).reshape(N, nb * 36).contiguous()
+    x = torch.randn(K, generator=g, device=device, dtype=torch.float32)
+    return {"N": N, "K": K, "blocks": blocks, "x": x, "seed": seed}
