@@ -29,43 +29,76 @@ hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const v
 }
 
 // out[i] = round(sum_{p=0}^{S-1} ws[p*MN + i]), summed in ascending p in float32
-// and rounded once (page "mlx PR 4682": separate accumulate kernel, one rounding).
-template <int DT, bool VEC>
-__global__ __launch_bounds__(256) void splitk_accum_kernel(const float* __restrict__ ws, void* __restrict__ out,
-                                                           int S, size_t MN) {
-    const size_t i0 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+// and rounded once (page "mlx PR 4682": separate accumulate kernel, one
+// rounding).  S is a template parameter so every partial load of a thread is
+// issued before the first add; one wave per work-group spreads the few
+// thousand threads over all CUs.
+template <int DT, int S, bool VEC>
+__global__ __launch_bounds__(64) void splitk_accum_kernel(const float* __restrict__ ws, void* __restrict__ out,
+                                                          size_t MN) {
+    const size_t i0 = ((size_t)blockIdx.x * 64 + threadIdx.x) * 4;
     if (i0 >= MN) return;
     if (VEC && i0 + 4 <= MN) {
-        f32x4 acc = *reinterpret_cast<const f32x4*>(ws + i0);
+        f32x4 v[S];
+#pragma unroll
+        for (int p = 0; p < S; ++p) v[p] = *reinterpret_cast<const f32x4*>(ws + (size_t)p * MN + i0);
+        f32x4 acc = v[0];
+#pragma unroll
         for (int p = 1; p < S; ++p) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(ws + (size_t)p * MN + i0);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            acc.x += v[p].x; acc.y += v[p].y; acc.z += v[p].z; acc.w += v[p].w;
         }
-        store_elem<DT>(out, i0 + 0, acc.x);
-        store_elem<DT>(out, i0 + 1, acc.y);
-        store_elem<DT>(out, i0 + 2, acc.z);
-        store_elem<DT>(out, i0 + 3, acc.w);
+        if constexpr (DT == DT_F16 || DT == DT_BF16) {
+            const uint32_t lo = DT == DT_F16 ? (f32_to_f16_bits(acc.x) | (f32_to_f16_bits(acc.y) << 16))
+                                             : (f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16));
+            const uint32_t hi = DT == DT_F16 ? (f32_to_f16_bits(acc.z) | (f32_to_f16_bits(acc.w) << 16))
+                                             : (f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16));
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + i0) = u32x2{lo, hi};
+        }
     } else {
         const size_t iend = i0 + 4 < MN ? i0 + 4 : MN;
         for (size_t i = i0; i < iend; ++i) {
             float acc = ws[i];
+#pragma unroll
             for (int p = 1; p < S; ++p) acc += ws[(size_t)p * MN + i];
             store_elem<DT>(out, i, acc);
         }
     }
 }
 
-hipError_t launch_splitk_accum(const float* ws, void* out, int splits, size_t MN, int dt, hipStream_t st) {
+template <int DT, int S>
+static void accum_go(const float* ws, void* out, size_t MN, bool vec, hipStream_t st) {
     const size_t threads = (MN + 3) / 4;
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    const bool vec = (MN % 4) == 0;
-    if (dt == DT_F16) {
-        if (vec) hipLaunchKernelGGL((splitk_accum_kernel<DT_F16, true>), grid, block, 0, st, ws, out, splits, MN);
-        else hipLaunchKernelGGL((splitk_accum_kernel<DT_F16, false>), grid, block, 0, st, ws, out, splits, MN);
-    } else {
-        if (vec) hipLaunchKernelGGL((splitk_accum_kernel<DT_BF16, true>), grid, block, 0, st, ws, out, splits, MN);
-        else hipLaunchKernelGGL((splitk_accum_kernel<DT_BF16, false>), grid, block, 0, st, ws, out, splits, MN);
+    const dim3 grid((unsigned)((threads + 63) / 64)), block(64);
+    if (vec) hipLaunchKernelGGL((splitk_accum_kernel<DT, S, true>), grid, block, 0, st, ws, out, MN);
+    else hipLaunchKernelGGL((splitk_accum_kernel<DT, S, false>), grid, block, 0, st, ws, out, MN);
+}
+
+template <int DT>
+static void accum_dt(const float* ws, void* out, int splits, size_t MN, bool vec, hipStream_t st) {
+    switch (splits) {
+        case 2: accum_go<DT, 2>(ws, out, MN, vec, st); break;
+        case 3: accum_go<DT, 3>(ws, out, MN, vec, st); break;
+        case 4: accum_go<DT, 4>(ws, out, MN, vec, st); break;
+        case 5: accum_go<DT, 5>(ws, out, MN, vec, st); break;
+        case 6: accum_go<DT, 6>(ws, out, MN, vec, st); break;
+        case 7: accum_go<DT, 7>(ws, out, MN, vec, st); break;
+        case 8: accum_go<DT, 8>(ws, out, MN, vec, st); break;
+        case 9: accum_go<DT, 9>(ws, out, MN, vec, st); break;
+        case 10: accum_go<DT, 10>(ws, out, MN, vec, st); break;
+        case 11: accum_go<DT, 11>(ws, out, MN, vec, st); break;
+        case 12: accum_go<DT, 12>(ws, out, MN, vec, st); break;
+        case 13: accum_go<DT, 13>(ws, out, MN, vec, st); break;
+        case 14: accum_go<DT, 14>(ws, out, MN, vec, st); break;
+        case 15: accum_go<DT, 15>(ws, out, MN, vec, st); break;
+        default: accum_go<DT, 16>(ws, out, MN, vec, st); break;
     }
+}
+
+hipError_t launch_splitk_accum(const float* ws, void* out, int splits, size_t MN, int dt, hipStream_t st) {
+    // the vector path needs 16-byte aligned partial rows and 8-byte aligned output
+    const bool vec = (MN % 4) == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0;
+    if (dt == DT_F16) accum_dt<DT_F16>(ws, out, splits, MN, vec, st);
+    else accum_dt<DT_BF16>(ws, out, splits, MN, vec, st);
     return hipGetLastError();
 }
 

@@ -8,23 +8,32 @@
 // split-K writes float32 partials that a separate kernel sums.
 //
 // gfx950 mapping:
-// * A work-group of 4 waves owns an output tile of BM = 16*MT rows of x by
-//   BN = 128 columns of W (each wave 2 fragments of 16 columns) and a range
-//   of 128-column K blocks.  LDS holds two buffers of: the x block (BM x 128,
-//   16-bit), the packed W block (128 rows x 128 codes), per-row group sums
-//   of x and the block's scales/biases converted to float32.
-// * Codes stay packed in LDS and are expanded in registers right before the
-//   MFMA into exact 16-bit integers: (field | 0x4300) is the bf16 value
-//   128 + q and (field | 0x6400) the f16 value 1024 + q, so each pair of
-//   codes costs one and/or.  The constant offset OFF*sum(x) this adds is
-//   removed in the group epilogue.  The codes of a word come out in the
-//   order 0,4,1,5,2,6,3,7 (8-bit: 0,2,1,3); x is written to LDS in the same
-//   order, and since both MFMA operands see the same permutation of k the
-//   dot product is unchanged.
+// * A work-group of 8 waves owns an output tile of BM = 16*MT rows of x by
+//   BN = 128 columns of W and a range of 128-column K blocks (4 MFMA k-steps
+//   each).  Waves 0-3 each own 2 fragments of 16 columns and take k-steps
+//   0-1 of every block; waves 4-7 own the same columns and take k-steps 2-3.
+//   The two halves add their float32 tiles through LDS once at the end, so a
+//   CU runs two waves per SIMD without splitting K further across
+//   work-groups (which would cost HBM traffic for partials).
+// * Packed weights are used by exactly one wave, so they go straight from
+//   HBM into that wave's MFMA B-operand registers through a 4-deep register
+//   ring (three blocks in flight while one is consumed); they never touch LDS.
+// * x is shared by the 4 waves: it is prefetched two blocks ahead into
+//   registers, written to one of two LDS buffers in the k order the code
+//   expansion produces, and read back as MFMA A operands; the block's
+//   scales/biases are staged alongside in float32.  One barrier per K block.
+// * Codes are expanded in registers right before the MFMA into exact 16-bit
+//   integers: one v_perm per pair of codes sets a magic exponent byte above
+//   two byte-aligned fields (0x43qq is the bf16 value 128 + q, 0x64qq the f16
+//   value 1024 + q).  The constant offset OFF*sum(x) this adds is removed in
+//   the group epilogue.  The codes come out in a fixed permutation of k; x
+//   is written to LDS in the same order, and since both MFMA operands see the
+//   same permutation the dot product is unchanged.
 // * MFMA v_mfma_f32_16x16x32_{bf16,f16}: A = x fragment (16 rows of M),
 //   B = W codes (16 columns of N).  A group of GS codes is GS/32 MFMA k-steps
-//   accumulated into a fresh float32 tile; the epilogue then adds
-//   scale * (tile) + (bias - OFF*scale) * sum(x) in float32.  Scale and bias
+//   accumulated into a fresh float32 tile; the same A fragments against an
+//   all-ones B give the group's row sums of x in a matching tile, and the
+//   epilogue adds scale * (tile) + (bias - OFF*scale) * (row sums) in float32.  Scale and bias
 //   never pass through a 16-bit format, so the output's only roundings are
 //   float32 accumulation and the final store.
 // * Work-groups are numbered so that the ones sharing a K range (and so the
@@ -44,19 +53,21 @@ struct QmmCfg {
     static constexpr int KS = GS / 32;                       // MFMA k-steps per group
     static constexpr int XP = QMM_KB + 8;                    // x LDS row pitch (elements)
     static constexpr int WROW = QMM_KB * BITS / 32;          // words per W row per block
-    static constexpr int WP = WROW + 4;                      // W LDS row pitch (words)
-    static constexpr int WPL = (S * BITS / 32) > 0 ? (S * BITS / 32) : 1;  // words per lane per group
-    static constexpr int X_BYTES = BM * XP * 2;
-    static constexpr int W_BYTES = QMM_BN * WP * 4;
-    static constexpr int XS_BYTES = GPB * BM * 4;
+    static constexpr int WPS = BITS == 8 ? 2 : 1;            // words a lane loads per k-step
+    static constexpr int WRING = 4;                          // register ring depth for W
+    static constexpr int XPR = QMM_KB / 8;                   // 16-byte x pieces per row per block
+    static constexpr int XPT = (MT * 16 * XPR + QMM_THREADS - 1) / QMM_THREADS;  // pieces per thread
+    static constexpr int XROWS = XPT * QMM_THREADS / XPR;    // x rows held in LDS (>= BM)
+    static constexpr int X_BYTES = XROWS * XP * 2;
     static constexpr int SB_BYTES = 2 * GPB * QMM_BN * 4;
-    static constexpr int BUF_BYTES = X_BYTES + W_BYTES + XS_BYTES + SB_BYTES;
-    static constexpr int W_PIECES = BITS / 2;                // 16-byte W pieces per thread per block
-    static constexpr int SB_PER_THREAD = GPB >= 2 ? GPB / 2 : 1;
-    static constexpr uint32_t MAGIC = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    static constexpr int BUF_BYTES = X_BYTES + SB_BYTES;
+    static constexpr int SB_SLICES = QMM_THREADS / QMM_BN;   // thread slices over the groups of a block
     static constexpr float OFF = (DT == DT_F16) ? 1024.f : (BITS == 8 ? 0.f : 128.f);
+    static constexpr int RED_BYTES = QMM_WAVES_N * MT * QMM_NB * 4 * 64 * 4;
     static_assert(BUF_BYTES % 16 == 0, "buffer alignment");
     static_assert(2 * BUF_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(RED_BYTES <= 2 * BUF_BYTES, "end reduction reuses the LDS buffers");
+    static_assert(GPB <= SB_SLICES, "one scale/bias slice per group");
 };
 
 template <int DT>
@@ -69,68 +80,84 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// 8 codes of one unit as 16-bit MFMA operands.  4-bit: one word, pairs
-// (i, i+4).  2-bit: 16 bits v, spread so codes 4..7 land in the high half.
-// 8-bit: two words, pairs (0,2), (1,3), (4,6), (5,7).
+// 8 codes of one unit as 16-bit MFMA operands (exact integers).  The word
+// is split into byte-aligned fields and one v_perm per pair puts two field
+// bytes under the magic exponent byte: 0x43qq is the bf16 value 128 + q and
+// 0x64qq the f16 value 1024 + q.  Element orders of the 8 operand slots:
+//   4-bit: 0,2,4,6,1,3,5,7   (low nibbles, then high nibbles, of one word)
+//   2-bit: 0,4,1,5,2,6,3,7   (fields t of the unit's two bytes)
+//   8-bit: 0..7              (bytes of two words; bf16 converts, since 128 + q
+//                             would overflow the bf16 mantissa for q >= 128)
+__device__ constexpr uint32_t perm_sel(int i, int j) {   // bytes i, j of the field word under the magic byte
+    return (uint32_t)i | (4u << 8) | ((uint32_t)j << 16) | (4u << 24);
+}
+
 template <int DT, int BITS>
 __device__ __forceinline__ u32x4 unpack_unit(uint32_t w0, uint32_t w1) {
-    constexpr uint32_t MAGIC = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
     u32x4 r;
     if constexpr (BITS == 4) {
-        r.x = (w0 & 0x000f000fu) | MAGIC;
-        r.y = ((w0 >> 4) & 0x000f000fu) | MAGIC;
-        r.z = ((w0 >> 8) & 0x000f000fu) | MAGIC;
-        r.w = ((w0 >> 12) & 0x000f000fu) | MAGIC;
+        const uint32_t lo = w0 & 0x0f0f0f0fu, hi = (w0 >> 4) & 0x0f0f0f0fu;
+        r.x = __builtin_amdgcn_perm(MB, lo, perm_sel(0, 1));
+        r.y = __builtin_amdgcn_perm(MB, lo, perm_sel(2, 3));
+        r.z = __builtin_amdgcn_perm(MB, hi, perm_sel(0, 1));
+        r.w = __builtin_amdgcn_perm(MB, hi, perm_sel(2, 3));
     } else if constexpr (BITS == 2) {
-        const uint32_t t = w0 | (w0 << 8);   // w0 holds the unit in its low 16 bits
-        r.x = (t & 0x00030003u) | MAGIC;
-        r.y = ((t >> 2) & 0x00030003u) | MAGIC;
-        r.z = ((t >> 4) & 0x00030003u) | MAGIC;
-        r.w = ((t >> 6) & 0x00030003u) | MAGIC;
+        // w0 holds the unit in its low 16 bits: byte 0 = codes 0-3, byte 1 = codes 4-7
+        r.x = __builtin_amdgcn_perm(MB, w0 & 0x0303u, perm_sel(0, 1));
+        r.y = __builtin_amdgcn_perm(MB, (w0 >> 2) & 0x0303u, perm_sel(0, 1));
+        r.z = __builtin_amdgcn_perm(MB, (w0 >> 4) & 0x0303u, perm_sel(0, 1));
+        r.w = __builtin_amdgcn_perm(MB, (w0 >> 6) & 0x0303u, perm_sel(0, 1));
     } else if constexpr (DT == DT_F16) {
-        r.x = (w0 & 0x00ff00ffu) | MAGIC;
-        r.y = ((w0 >> 8) & 0x00ff00ffu) | MAGIC;
-        r.z = (w1 & 0x00ff00ffu) | MAGIC;
-        r.w = ((w1 >> 8) & 0x00ff00ffu) | MAGIC;
+        r.x = __builtin_amdgcn_perm(MB, w0, perm_sel(0, 1));
+        r.y = __builtin_amdgcn_perm(MB, w0, perm_sel(2, 3));
+        r.z = __builtin_amdgcn_perm(MB, w1, perm_sel(0, 1));
+        r.w = __builtin_amdgcn_perm(MB, w1, perm_sel(2, 3));
     } else {
         // bf16 holds every integer up to 256 exactly: convert, keep the upper half.
         auto pair = [](uint32_t a, uint32_t b) {
-            return (__float_as_uint((float)a) >> 16) | (__float_as_uint((float)b) & 0xffff0000u);
+            return __builtin_amdgcn_perm(__float_as_uint((float)b), __float_as_uint((float)a), 0x07060302u);
         };
-        r.x = pair(w0 & 0xffu, (w0 >> 16) & 0xffu);
-        r.y = pair((w0 >> 8) & 0xffu, w0 >> 24);
-        r.z = pair(w1 & 0xffu, (w1 >> 16) & 0xffu);
-        r.w = pair((w1 >> 8) & 0xffu, w1 >> 24);
+        r.x = pair(w0 & 0xffu, (w0 >> 8) & 0xffu);
+        r.y = pair((w0 >> 16) & 0xffu, w0 >> 24);
+        r.z = pair(w1 & 0xffu, (w1 >> 8) & 0xffu);
+        r.w = pair((w1 >> 16) & 0xffu, w1 >> 24);
     }
     return r;
 }
 
-// Eight consecutive x values (d = x0x1, x2x3, x4x5, x6x7) in the unit order
-// used by unpack_unit.
+// Eight consecutive 16-bit x values (d = x0x1, x2x3, x4x5, x6x7) in the
+// slot order unpack_unit uses for BITS.
 template <int BITS>
 __device__ __forceinline__ u32x4 permute_x(u32x4 d) {
-    u32x4 r;
     if constexpr (BITS == 8) {
-        r.x = (d.x & 0xffffu) | (d.y << 16);
-        r.y = (d.x >> 16) | (d.y & 0xffff0000u);
-        r.z = (d.z & 0xffffu) | (d.w << 16);
-        r.w = (d.z >> 16) | (d.w & 0xffff0000u);
+        return d;
+    } else if constexpr (BITS == 4) {
+        // (x0,x2) (x4,x6) (x1,x3) (x5,x7)
+        return u32x4{__builtin_amdgcn_perm(d.y, d.x, 0x05040100u), __builtin_amdgcn_perm(d.w, d.z, 0x05040100u),
+                     __builtin_amdgcn_perm(d.y, d.x, 0x07060302u), __builtin_amdgcn_perm(d.w, d.z, 0x07060302u)};
     } else {
-        r.x = (d.x & 0xffffu) | (d.z << 16);
-        r.y = (d.x >> 16) | (d.z & 0xffff0000u);
-        r.z = (d.y & 0xffffu) | (d.w << 16);
-        r.w = (d.y >> 16) | (d.w & 0xffff0000u);
+        // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+        return u32x4{__builtin_amdgcn_perm(d.z, d.x, 0x05040100u), __builtin_amdgcn_perm(d.z, d.x, 0x07060302u),
+                     __builtin_amdgcn_perm(d.w, d.y, 0x05040100u), __builtin_amdgcn_perm(d.w, d.y, 0x07060302u)};
     }
-    return r;
 }
 
-template <int DT>
-__device__ __forceinline__ float sum8(u32x4 d) {
-    float t = half_lo<DT>(d.x) + half_hi<DT>(d.x);
-    t += half_lo<DT>(d.y) + half_hi<DT>(d.y);
-    t += half_lo<DT>(d.z) + half_hi<DT>(d.z);
-    t += half_lo<DT>(d.w) + half_hi<DT>(d.w);
-    return t;
+// WPL consecutive words at p (WPL = 1, 2, 4 or 8; 16-byte aligned for 4 and 8).
+template <int WPL>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&v)[WPL]) {
+    if constexpr (WPL == 1) {
+        v[0] = p[0];
+    } else if constexpr (WPL == 2) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+        v[0] = a.x; v[1] = a.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPL / 4; ++i) {
+            const u32x4 a = reinterpret_cast<const u32x4*>(p)[i];
+            v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+        }
+    }
 }
 
 template <int DT, int BITS, int GS, int MT, bool SPLIT>
@@ -154,80 +181,81 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const int nkb = K / QMM_KB;
     const int kb0 = (int)((long)split * nkb / splits);
     const int kb1 = (int)((long)(split + 1) * nkb / splits);
+    const int nk = kb1 - kb0;
     const int G = K / GS;
     const size_t row_words = (size_t)K * BITS / 32;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & (QMM_WAVES_N - 1);   // column slice of this wave
+    const int wk = wave / QMM_WAVES_N;          // k-step pair of this wave: steps 2wk, 2wk+1 of each block
     const int lrow = lane & 15, lgrp = lane >> 4;
 
-    u32x4 xr[MT];
-    u32x4 wr[C::W_PIECES];
-    float sr[C::SB_PER_THREAD], br[C::SB_PER_THREAD];
-    const int sb_col = tid & 127;
-    const int sb_g0 = (tid >> 7) * C::SB_PER_THREAD;
-    const bool sb_active = sb_g0 < C::GPB;
+    // ---- x (+ scales/biases) ring: 2 register slots -> 2 LDS buffers.
+    // Every prefetch load is unconditional, with the block index and the row
+    // and column indices clamped into range: rows of x past M and columns
+    // past N then only feed outputs that are never stored.  Loaded values are
+    // left untouched until they are written to LDS two blocks later, so the
+    // compiler never has to wait on a load it has just issued.
+    u32x4 xr[2][C::XPT];
+    uint32_t sr[2], br[2];
+    const int sb_col = tid % QMM_BN;
+    const int sb_g = tid / QMM_BN;
+    const bool sb_active = sb_g < C::GPB;
+    const int sb_n = min(n0 + sb_col, N - 1);
+    const int sb_gl = min(sb_g, C::GPB - 1);   // in-range group for inactive slices
 
-    auto gload = [&](int kb) {
+    auto x_gload = [&](int kb_req, int slot) {
+        const int kb = min(kb_req, kb1 - 1);
         const int k0 = kb * QMM_KB;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int m = m0 + (tid >> 4) + 16 * i;
-            if (m < M)
-                xr[i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + (size_t)m * K +
-                                                        k0 + 8 * (tid & 15));
-            else
-                xr[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < C::XPT; ++i) {
+            const int p = tid + QMM_THREADS * i;              // piece p: row p / XPR, unit p % XPR
+            const int m = min(m0 + p / C::XPR, M - 1);
+            xr[slot][i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + (size_t)m * K + k0 +
+                                                          8 * (p % C::XPR));
         }
+        const size_t gi = (size_t)sb_n * G + (size_t)kb * C::GPB + sb_gl;
+        sr[slot] = static_cast<const uint16_t*>(scales)[gi];
+        br[slot] = static_cast<const uint16_t*>(biases)[gi];
+    };
+
+    auto x_lstore = [&](int slot, int buf) {
+        unsigned char* base = smem + buf * C::BUF_BYTES;
+        uint16_t* xl = reinterpret_cast<uint16_t*>(base);
+        float* sbl = reinterpret_cast<float*>(base + C::X_BYTES);
 #pragma unroll
-        for (int i = 0; i < C::W_PIECES; ++i) {
+        for (int i = 0; i < C::XPT; ++i) {
             const int p = tid + QMM_THREADS * i;
-            const int n = n0 + p / BITS;
-            if (n < N)
-                wr[i] = *reinterpret_cast<const u32x4*>(w + (size_t)n * row_words + (size_t)kb * C::WROW +
-                                                        4 * (p % BITS));
-            else
-                wr[i] = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(xl + (p / C::XPR) * C::XP + 8 * (p % C::XPR)) = permute_x<BITS>(xr[slot][i]);
         }
-        const int n = n0 + sb_col;
-#pragma unroll
-        for (int j = 0; j < C::SB_PER_THREAD; ++j) {
-            if (sb_active && n < N) {
-                const size_t gi = (size_t)n * G + (size_t)kb * C::GPB + sb_g0 + j;
-                sr[j] = load_elem<DT>(scales, gi);
-                br[j] = load_elem<DT>(biases, gi);
-            } else {
-                sr[j] = 0.f;
-                br[j] = 0.f;
-            }
+        if (sb_active) {
+            const float sv = DT == DT_F16 ? f16_bits_to_f32(sr[slot]) : bf16_bits_to_f32(sr[slot]);
+            const float bv = DT == DT_F16 ? f16_bits_to_f32(br[slot]) : bf16_bits_to_f32(br[slot]);
+            sbl[sb_g * QMM_BN + sb_col] = sv;
+            sbl[(C::GPB + sb_g) * QMM_BN + sb_col] = fmaf(-C::OFF, sv, bv);
         }
     };
 
-    auto lstore = [&](int buf) {
-        unsigned char* base = smem + buf * C::BUF_BYTES;
-        uint16_t* xl = reinterpret_cast<uint16_t*>(base);
-        uint32_t* wl = reinterpret_cast<uint32_t*>(base + C::X_BYTES);
-        float* xsl = reinterpret_cast<float*>(base + C::X_BYTES + C::W_BYTES);
-        float* sbl = reinterpret_cast<float*>(base + C::X_BYTES + C::W_BYTES + C::XS_BYTES);
-        const int u = tid & 15;
+    // ---- W ring: WRING register slots of this wave's B-operand words (2 k-steps)
+    // code offset (within the block) of this lane's unit in k-step s
+    auto unit_code = [&](int s) { return (s / C::KS) * GS + lgrp * C::S + 8 * (s % C::KS); };
+    uint32_t wr[C::WRING][NB][2][C::WPS];
+    auto w_gload = [&](int kb_req, int slot) {
+        const int kb = min(kb_req, kb1 - 1);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int row = (tid >> 4) + 16 * i;
-            *reinterpret_cast<u32x4*>(xl + row * C::XP + 8 * u) = permute_x<BITS>(xr[i]);
-            float t = sum8<DT>(xr[i]);
+        for (int nf = 0; nf < NB; ++nf) {
+            const int n = min(n0 + wn * (NB * 16) + nf * 16 + lrow, N - 1);
+            const uint32_t* row = w + (size_t)n * row_words + (size_t)kb * C::WROW;
 #pragma unroll
-            for (int off = 1; off < GS / 8; off <<= 1) t += __shfl_xor(t, off, 64);
-            if ((u % (GS / 8)) == 0) xsl[(u / (GS / 8)) * C::BM + row] = t;
-        }
-#pragma unroll
-        for (int i = 0; i < C::W_PIECES; ++i) {
-            const int p = tid + QMM_THREADS * i;
-            *reinterpret_cast<u32x4*>(wl + (p / BITS) * C::WP + 4 * (p % BITS)) = wr[i];
-        }
-        if (sb_active) {
-#pragma unroll
-            for (int j = 0; j < C::SB_PER_THREAD; ++j) {
-                sbl[(sb_g0 + j) * QMM_BN + sb_col] = sr[j];
-                sbl[(C::GPB + sb_g0 + j) * QMM_BN + sb_col] = fmaf(-C::OFF, sr[j], br[j]);
+            for (int st = 0; st < 2; ++st) {
+                const int word = unit_code(2 * wk + st) * BITS / 32;
+                if constexpr (C::WPS == 2) {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(row + word);
+                    wr[slot][nf][st][0] = v.x;
+                    wr[slot][nf][st][1] = v.y;
+                } else {
+                    wr[slot][nf][st][0] = row[word];
+                }
             }
         }
     };
@@ -238,100 +266,131 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
         for (int nf = 0; nf < NB; ++nf) run[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf) {
+    constexpr uint32_t ONE2 = DT == DT_F16 ? 0x3c003c00u : 0x3f803f80u;
+    const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
+
+    auto compute = [&](int buf, int wslot) {
         const unsigned char* base = smem + buf * C::BUF_BYTES;
         const uint16_t* xl = reinterpret_cast<const uint16_t*>(base);
-        const uint32_t* wl = reinterpret_cast<const uint32_t*>(base + C::X_BYTES);
-        const float* xsl = reinterpret_cast<const float*>(base + C::X_BYTES + C::W_BYTES);
-        const float* sbl = reinterpret_cast<const float*>(base + C::X_BYTES + C::W_BYTES + C::XS_BYTES);
+        const float* sbl = reinterpret_cast<const float*>(base + C::X_BYTES);
+        // expand this wave's two k-steps of codes once
+        u32x4 bf[2][NB];
+        int off[2];
 #pragma unroll
-        for (int gi = 0; gi < C::GPB; ++gi) {
-            uint32_t bw[NB][C::WPL];
+        for (int st = 0; st < 2; ++st) {
+            const int c = unit_code(2 * wk + st);
+            off[st] = c;
 #pragma unroll
             for (int nf = 0; nf < NB; ++nf) {
-                const int row = wave * (NB * 16) + nf * 16 + lrow;
-                int word;
-                if constexpr (BITS == 2 && GS == 32) word = gi * 2 + (lgrp >> 1);
-                else word = (gi * GS + lgrp * C::S) * BITS / 32;
-#pragma unroll
-                for (int i = 0; i < C::WPL; ++i) bw[nf][i] = wl[row * C::WP + word + i];
+                const uint32_t* bw = wr[wslot][nf][st];
+                if constexpr (BITS == 4) {
+                    bf[st][nf] = unpack_unit<DT, 4>(bw[0], 0u);
+                } else if constexpr (BITS == 8) {
+                    bf[st][nf] = unpack_unit<DT, 8>(bw[0], bw[1]);
+                } else {
+                    bf[st][nf] = unpack_unit<DT, 2>((bw[0] >> (16 * ((c >> 3) & 1))) & 0xffffu, 0u);
+                }
             }
-            f32x4 gacc[MT][NB];
+        }
+        // the two k-steps share one group unless a group is a single k-step
+        constexpr int NG = C::KS >= 2 ? 1 : 2;
+        float sv[NG][NB], bv[NG][NB];
 #pragma unroll
-            for (int mf = 0; mf < MT; ++mf)
+        for (int gp = 0; gp < NG; ++gp) {
+            const int g = (2 * wk + gp) / C::KS;
 #pragma unroll
-                for (int nf = 0; nf < NB; ++nf) gacc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nf = 0; nf < NB; ++nf) {
+                const int col = wn * (NB * 16) + nf * 16 + lrow;
+                sv[gp][nf] = sbl[g * QMM_BN + col];
+                bv[gp][nf] = sbl[(C::GPB + g) * QMM_BN + col];
+            }
+        }
+        // one 16-row fragment of x at a time keeps one row of group tiles live; the
+        // group's row sums of x come from one more MFMA against ones
 #pragma unroll
-            for (int t = 0; t < C::KS; ++t) {
-                u32x4 bf[NB];
+        for (int mf = 0; mf < MT; ++mf) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xl + (mf * 16 + lrow) * C::XP + off[0]);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xl + (mf * 16 + lrow) * C::XP + off[1]);
+#pragma unroll
+            for (int gp = 0; gp < NG; ++gp) {
+                f32x4 gacc[NB];
 #pragma unroll
                 for (int nf = 0; nf < NB; ++nf) {
-                    if constexpr (BITS == 4) {
-                        bf[nf] = unpack_unit<DT, 4>(bw[nf][t], 0u);
-                    } else if constexpr (BITS == 8) {
-                        bf[nf] = unpack_unit<DT, 8>(bw[nf][2 * t], bw[nf][2 * t + 1]);
+                    if constexpr (NG == 1) {
+                        gacc[nf] = mfma16x16x32<DT>(a0, bf[0][nf], f32x4{0.f, 0.f, 0.f, 0.f});
+                        gacc[nf] = mfma16x16x32<DT>(a1, bf[1][nf], gacc[nf]);
                     } else {
-                        const int half = (GS == 32) ? (lgrp & 1) : (t & 1);
-                        const uint32_t wd = (GS == 32) ? bw[nf][0] : bw[nf][t >> 1];
-                        bf[nf] = unpack_unit<DT, 2>((wd >> (16 * half)) & 0xffffu, 0u);
+                        gacc[nf] = mfma16x16x32<DT>(gp ? a1 : a0, bf[gp][nf], f32x4{0.f, 0.f, 0.f, 0.f});
                     }
                 }
-#pragma unroll
-                for (int mf = 0; mf < MT; ++mf) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        xl + (mf * 16 + lrow) * C::XP + gi * GS + lgrp * C::S + 8 * t);
-#pragma unroll
-                    for (int nf = 0; nf < NB; ++nf) gacc[mf][nf] = mfma16x16x32<DT>(a, bf[nf], gacc[mf][nf]);
+                f32x4 gxs;
+                if constexpr (NG == 1) {
+                    gxs = mfma16x16x32<DT>(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+                    gxs = mfma16x16x32<DT>(a1, ones, gxs);
+                } else {
+                    gxs = mfma16x16x32<DT>(gp ? a1 : a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
                 }
-            }
-            float sv[NB], bv[NB];
-#pragma unroll
-            for (int nf = 0; nf < NB; ++nf) {
-                const int col = wave * (NB * 16) + nf * 16 + lrow;
-                sv[nf] = sbl[gi * QMM_BN + col];
-                bv[nf] = sbl[(C::GPB + gi) * QMM_BN + col];
-            }
-#pragma unroll
-            for (int mf = 0; mf < MT; ++mf) {
-                const f32x4 xs4 = *reinterpret_cast<const f32x4*>(xsl + gi * C::BM + mf * 16 + 4 * lgrp);
 #pragma unroll
                 for (int nf = 0; nf < NB; ++nf)
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        run[mf][nf][v] = fmaf(sv[nf], gacc[mf][nf][v], fmaf(bv[nf], xs4[v], run[mf][nf][v]));
+                        run[mf][nf][v] = fmaf(sv[gp][nf], gacc[nf][v], fmaf(bv[gp][nf], gxs[v], run[mf][nf][v]));
             }
         }
     };
 
-    if (kb0 < kb1) {
-        gload(kb0);
-        lstore(0);
-        if (kb0 + 1 < kb1) gload(kb0 + 1);
+    if (nk > 0) {
+        x_gload(kb0, 0);
+        x_gload(kb0 + 1, 1);
+#pragma unroll
+        for (int i = 0; i < C::WRING; ++i) w_gload(kb0 + i, i);
+        x_lstore(0, 0);
+        x_gload(kb0 + 2, 0);
         __syncthreads();
-        for (int kb = kb0; kb < kb1; ++kb) {
-            const int buf = (kb - kb0) & 1;
-            compute(buf);
-            if (kb + 1 < kb1) {
-                lstore(buf ^ 1);
-                if (kb + 2 < kb1) gload(kb + 2);
+        // Block i: compute from LDS buffer i%2 and W slot i%4; then stage x(i+1)
+        // into the other buffer and request x(i+3) and W(i+4) into the freed
+        // slots.  Past the last block the requests repeat the last block and
+        // the staged data is never read.
+        for (int base = 0; base < nk; base += C::WRING) {
+#pragma unroll
+            for (int j = 0; j < C::WRING; ++j) {
+                const int i = base + j;
+                if (i < nk) compute(j & 1, j);
+                x_lstore((j + 1) & 1, (j + 1) & 1);
+                x_gload(kb0 + i + 3, (j + 1) & 1);
+                w_gload(kb0 + i + C::WRING, j);
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 
+    // add the second half's tiles to the first half's, then store
+    float* red = reinterpret_cast<float*>(smem);
+    if (wk == 1) {
+#pragma unroll
+        for (int mf = 0; mf < MT; ++mf)
+#pragma unroll
+            for (int nf = 0; nf < NB; ++nf)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane] = run[mf][nf][v];
+    }
+    __syncthreads();
+    if (wk == 1) return;
 #pragma unroll
     for (int mf = 0; mf < MT; ++mf)
 #pragma unroll
         for (int nf = 0; nf < NB; ++nf)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
+                const float r = run[mf][nf][v] + red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane];
                 const int m = m0 + mf * 16 + 4 * lgrp + v;
-                const int n = n0 + wave * (NB * 16) + nf * 16 + lrow;
+                const int n = n0 + wn * (NB * 16) + nf * 16 + lrow;
                 if (m < M && n < N) {
                     if constexpr (SPLIT)
-                        ws[((size_t)split * M + m) * N + n] = run[mf][nf][v];
+                        ws[((size_t)split * M + m) * N + n] = r;
                     else
-                        store_elem<DT>(out, (size_t)m * N + n, run[mf][nf][v]);
+                        store_elem<DT>(out, (size_t)m * N + n, r);
                 }
             }
 }

@@ -6,16 +6,105 @@
 // held in registers and reused across the rows a wave owns, float32
 // accumulators, and a cross-lane reduction followed by one store per output.
 //
-// gfx950 mapping: one wave64 per work-group owns QMV_ROWS consecutive rows
-// of W and up to MT rows of x.  A row of W is cut into 16-byte chunks; lane
-// l takes chunks l, l+64, ... so every wave-wide load is 1 KB of one row,
-// contiguous.  Small single-wave work-groups keep the per-CU load even when
-// N/QMV_ROWS is not a multiple of the CU count.  The final reduction is a
-// fixed xor-butterfly, so results do not change from run to run.
+// gfx950 mapping:
+// * A wave owns QMV_ROWS consecutive rows of W and up to MT rows of x, and
+//   a contiguous range of the row's 16-byte chunks; lane l takes chunks
+//   l, l+64, ... of that range, so each wave-wide load reads 1 KB of one row.
+//   When N alone gives too few waves to cover the chip, KSPLIT waves of one
+//   work-group split the chunks of the same rows and their partial sums are
+//   added in LDS in a fixed order.
+// * 16-bit x: a word is split into byte-aligned fields and one v_perm per
+//   pair of codes sets a magic exponent byte above two of them (0x43qq is the
+//   bf16 value 128+q, 0x64qq the f16 value 1024+q; f16 then subtracts 1024
+//   exactly), so codes become exact 16-bit integers contracted with
+//   v_dot2_f32_{bf16,f16} two at a time.  The bf16 offset adds 128*sum(x),
+//   removed by using bias - 128*scale in the group epilogue.  x is paired in
+//   the same element order with v_perm.  float32 x (and 8-bit codes with
+//   bf16 x) use per-code conversion and float32 FMA.
+// * The final reductions are fixed xor-butterflies, so results do not change
+//   from run to run.
 #include "qmx_device.h"
 #include "qmx_internal.h"
 
 namespace qmx {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+}
+
+// The 16-bit code pairs of a word.  The word is first split into
+// byte-aligned fields (4-bit: low nibbles = codes 0,2,4,6 and high nibbles =
+// codes 1,3,5,7; 2-bit: field t of every byte = codes t, t+4, t+8, t+12;
+// 8-bit: the bytes themselves), then one v_perm per pair puts two field bytes
+// under the magic exponent byte: 0x43 makes the bf16 value 128 + q, 0x64 the
+// f16 value 1024 + q, from which f16 subtracts 1024 exactly.
+template <int BITS>
+struct PairOrder {
+    // element index (within the word) of the first / second code of pair k
+    __device__ static constexpr int first(int k) {
+        return BITS == 4 ? (k < 2 ? 4 * k : 4 * (k - 2) + 1)
+             : BITS == 2 ? ((k & 1) ? 8 + (k >> 1) : (k >> 1))
+             : 2 * k;
+    }
+    __device__ static constexpr int second(int k) { return first(k) + (BITS == 4 ? 2 : BITS == 2 ? 4 : 1); }
+};
+
+// v_perm_b32 selector taking bytes i and j of the second operand (the field
+// word) and byte 0 of the first (the magic byte), as (lo16, hi16) = (i, j).
+__device__ constexpr uint32_t magic_sel(int i, int j) {
+    return (uint32_t)i | (4u << 8) | ((uint32_t)j << 16) | (4u << 24);
+}
+
+template <int DT, int BITS>
+__device__ __forceinline__ void code_pairs(uint32_t w, uint32_t (&q)[16 / BITS]) {
+    constexpr uint32_t MB = DT == DT_BF16 ? 0x43434343u : 0x64646464u;
+    if constexpr (BITS == 4) {
+        const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+        q[0] = __builtin_amdgcn_perm(MB, lo, magic_sel(0, 1));
+        q[1] = __builtin_amdgcn_perm(MB, lo, magic_sel(2, 3));
+        q[2] = __builtin_amdgcn_perm(MB, hi, magic_sel(0, 1));
+        q[3] = __builtin_amdgcn_perm(MB, hi, magic_sel(2, 3));
+    } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t f = (w >> (2 * t)) & 0x03030303u;
+            q[2 * t] = __builtin_amdgcn_perm(MB, f, magic_sel(0, 1));
+            q[2 * t + 1] = __builtin_amdgcn_perm(MB, f, magic_sel(2, 3));
+        }
+    } else {
+        q[0] = __builtin_amdgcn_perm(MB, w, magic_sel(0, 1));
+        q[1] = __builtin_amdgcn_perm(MB, w, magic_sel(2, 3));
+    }
+    if constexpr (DT == DT_F16) {
+#pragma unroll
+        for (int k = 0; k < 16 / BITS; ++k) {
+            const h2_t v = __builtin_bit_cast(h2_t, q[k]) - h2_t{(_Float16)1024.f, (_Float16)1024.f};
+            q[k] = __builtin_bit_cast(uint32_t, v);
+        }
+    }
+}
+
+// x values a and b (element indices within the word, whose 16-bit values sit
+// two per dword in d) as one (lo, hi) pair.
+__device__ __forceinline__ uint32_t x_pair(const uint32_t* d, int a, int b) {
+    const uint32_t sa = (a & 1) ? 2u : 0u, sb = (b & 1) ? 6u : 4u;
+    const uint32_t sel = sa | ((sa + 1) << 8) | (sb << 16) | ((sb + 1) << 24);
+    return __builtin_amdgcn_perm(d[b >> 1], d[a >> 1], sel);
+}
+
+// Offset that code_pairs leaves on every code.
+template <int DT>
+constexpr float code_offset() { return DT == DT_BF16 ? 128.f : 0.f; }
+
+template <int DT, int BITS>
+constexpr bool use_dot2() { return DT != DT_F32 && (BITS != 8 || DT == DT_F16); }
 
 // Expand one packed word into its 32/BITS codes (element order), as float.
 template <int BITS>
@@ -41,61 +130,195 @@ __device__ __forceinline__ void unpack_word(uint32_t w, float (&q)[32 / BITS]) {
     }
 }
 
-// The N values of x starting at element index `idx` (idx*sizeof aligned to
-// 16 bytes for f32 / 8 bytes for 16-bit types), as float.
-template <int DT, int N>
-__device__ __forceinline__ void load_x(const void* x, size_t idx, float (&v)[N]) {
-    if constexpr (DT == DT_F32) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + idx);
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const u32x4 d = p[i];
-            v[4 * i + 0] = __uint_as_float(d.x);
-            v[4 * i + 1] = __uint_as_float(d.y);
-            v[4 * i + 2] = __uint_as_float(d.z);
-            v[4 * i + 3] = __uint_as_float(d.w);
-        }
-    } else if constexpr (N % 8 == 0) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + idx);
-#pragma unroll
-        for (int i = 0; i < N / 8; ++i) {
-            const u32x4 d = p[i];
-            const uint32_t ws[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = half_lo<DT>(ws[j]);
-                v[8 * i + 2 * j + 1] = half_hi<DT>(ws[j]);
-            }
-        }
-    } else {
-        static_assert(N == 4, "x word width");
-        const u32x2 d = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(x) + idx);
-        v[0] = half_lo<DT>(d.x);
-        v[1] = half_hi<DT>(d.x);
-        v[2] = half_lo<DT>(d.y);
-        v[3] = half_hi<DT>(d.y);
-    }
+// Registers of one chunk: the R rows' 16-byte weight chunks, their scales and
+// biases (raw storage bits), and the MT rows' x values under the chunk.
+template <int DT, int BITS, int GS, int MT>
+struct QmvStage {
+    static constexpr int R = QMV_ROWS;
+    static constexpr int CPC = 128 / BITS;
+    static constexpr int PARTS = CPC > GS ? CPC / GS : 1;
+    static constexpr int XQ = CPC * (DT == DT_F32 ? 4 : 2) / 16;   // 16-byte x pieces per chunk
+    u32x4 w[R];
+    uint32_t s[R][PARTS], b[R][PARTS];
+    u32x4 x[MT][XQ];
+};
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
+    if constexpr (DT == DT_F32) return static_cast<const uint32_t*>(p)[i];
+    else return static_cast<const uint16_t*>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_to_f32(uint32_t v) {
+    if constexpr (DT == DT_F32) return __uint_as_float(v);
+    else if constexpr (DT == DT_F16) return f16_bits_to_f32(v);
+    else return bf16_bits_to_f32(v);
 }
 
 template <int DT, int BITS, int GS, int MT>
-__global__ __launch_bounds__(64) void qmv_kernel(const uint32_t* __restrict__ w,
-                                                 const void* __restrict__ scales,
-                                                 const void* __restrict__ biases,
-                                                 const void* __restrict__ x,
-                                                 void* __restrict__ out, int M, int N, int K) {
-    constexpr int R = QMV_ROWS;
-    constexpr int CPW = 32 / BITS;                 // codes per word
-    constexpr int CPC = 4 * CPW;                   // codes per 16-byte chunk
-    constexpr int PARTS = CPC > GS ? CPC / GS : 1; // groups touched by one chunk
-    constexpr int WPP = 4 / PARTS;                 // words per group part
+__device__ __forceinline__ void qmv_load(QmvStage<DT, BITS, GS, MT>& st, const uint32_t* __restrict__ w,
+                                         const void* __restrict__ scales, const void* __restrict__ biases,
+                                         const void* __restrict__ x, int c, int n0, int N, int m0, int mcount,
+                                         int K, int G, size_t row_words) {
+    using S = QmvStage<DT, BITS, GS, MT>;
+    const int g0 = (c * S::CPC) / GS;
+#pragma unroll
+    for (int r = 0; r < S::R; ++r) {
+        const int n = min(n0 + r, N - 1);   // rows past N are computed but never stored
+        st.w[r] = *reinterpret_cast<const u32x4*>(w + (size_t)n * row_words + 4 * (size_t)c);
+#pragma unroll
+        for (int p = 0; p < S::PARTS; ++p) {
+            const size_t gi = (size_t)n * G + g0 + p;
+            st.s[r][p] = load_raw<DT>(scales, gi);
+            st.b[r][p] = load_raw<DT>(biases, gi);
+        }
+    }
+    constexpr int EB = DT == DT_F32 ? 4 : 2;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int mm = m < mcount ? m : 0;   // rows past M reuse row m0; never stored
+        const unsigned char* xp = static_cast<const unsigned char*>(x) +
+                                  ((size_t)(m0 + mm) * K + (size_t)c * S::CPC) * EB;
+#pragma unroll
+        for (int i = 0; i < S::XQ; ++i) st.x[m][i] = reinterpret_cast<const u32x4*>(xp)[i];
+    }
+}
 
-    const int lane = threadIdx.x;
+// Word j (0..3) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t word_of(const u32x4& v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+template <int DT, int BITS, int GS, int MT>
+__device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st,
+                                            float (&acc)[QMV_ROWS][MT]) {
+    using S = QmvStage<DT, BITS, GS, MT>;
+    constexpr int R = S::R;
+    constexpr int PARTS = S::PARTS;
+    constexpr int WPP = 4 / PARTS;          // words per group part
+    constexpr int CPW = 32 / BITS;          // codes per word
+
+    float qd[R][MT][PARTS];
+    float xs[MT][PARTS];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p) {
+            xs[m][p] = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) qd[r][m][p] = 0.f;
+        }
+
+    if constexpr (use_dot2<DT, BITS>()) {
+        // Each word is split into byte-aligned fields (one code per byte); a
+        // v_perm places two of those bytes under the magic exponent byte,
+        // giving a pair of exact 16-bit codes, and x is paired the same way.
+        constexpr int PPW = CPW / 2;                       // pairs per word
+        constexpr uint32_t ONES = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+        uint32_t xp[MT][4][PPW];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            uint32_t d[S::XQ * 4];
+#pragma unroll
+            for (int i = 0; i < S::XQ; ++i) {
+                d[4 * i] = st.x[m][i].x; d[4 * i + 1] = st.x[m][i].y;
+                d[4 * i + 2] = st.x[m][i].z; d[4 * i + 3] = st.x[m][i].w;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t* dj = d + j * (CPW / 2);   // CPW values = CPW/2 dwords per word
+                float t = xs[m][j / WPP];
+#pragma unroll
+                for (int k = 0; k < PPW; ++k) {
+                    xp[m][j][k] = x_pair(dj, PairOrder<BITS>::first(k), PairOrder<BITS>::second(k));
+                    t = dot2<DT>(xp[m][j][k], ONES, t);
+                }
+                xs[m][j / WPP] = t;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t q[PPW];
+                code_pairs<DT, BITS>(word_of(st.w[r], j), q);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float t = qd[r][m][j / WPP];
+#pragma unroll
+                    for (int k = 0; k < PPW; ++k) t = dot2<DT>(q[k], xp[m][j][k], t);
+                    qd[r][m][j / WPP] = t;
+                }
+            }
+        }
+    } else {
+        // float32 path: x converted once per chunk, codes converted one by one
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float xv[MT][CPW];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                for (int e = 0; e < CPW; ++e) {
+                    const int idx = j * CPW + e;       // element within the chunk
+                    if constexpr (DT == DT_F32) {
+                        const u32x4 q4 = st.x[m][idx / 4];
+                        xv[m][e] = __uint_as_float(word_of(q4, idx % 4));
+                    } else {
+                        const u32x4 q4 = st.x[m][idx / 8];
+                        const uint32_t d = word_of(q4, (idx % 8) / 2);
+                        xv[m][e] = (idx & 1) ? half_hi<DT>(d) : half_lo<DT>(d);
+                    }
+                }
+                float t = 0.f;
+#pragma unroll
+                for (int e = 0; e < CPW; ++e) t += xv[m][e];
+                xs[m][j / WPP] += t;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float q[CPW];
+                unpack_word<BITS>(word_of(st.w[r], j), q);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float t = qd[r][m][j / WPP];
+#pragma unroll
+                    for (int e = 0; e < CPW; ++e) t = fmaf(q[e], xv[m][e], t);
+                    qd[r][m][j / WPP] = t;
+                }
+            }
+        }
+    }
+
+    constexpr float OFF = use_dot2<DT, BITS>() ? code_offset<DT>() : 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p) {
+            const float s = raw_to_f32<DT>(st.s[r][p]);
+            const float b = fmaf(-OFF, s, raw_to_f32<DT>(st.b[r][p]));
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] = fmaf(s, qd[r][m][p], fmaf(b, xs[m][p], acc[r][m]));
+        }
+}
+
+template <int DT, int BITS, int GS, int MT, int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __restrict__ w,
+                                                          const void* __restrict__ scales,
+                                                          const void* __restrict__ biases,
+                                                          const void* __restrict__ x,
+                                                          void* __restrict__ out, int M, int N, int K) {
+    constexpr int R = QMV_ROWS;
+    using S = QmvStage<DT, BITS, GS, MT>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * R;
     const int m0 = blockIdx.y * MT;
     const int mcount = min(MT, M - m0);
     const int G = K / GS;
-    const int chunks = K / CPC;
-    const size_t row_words = (size_t)(K / CPW);
+    const int chunks = K / S::CPC;
+    const size_t row_words = (size_t)K * BITS / 32;
+    const int c1 = (int)((long)(wave + 1) * chunks / KSPLIT);
 
     float acc[R][MT];
 #pragma unroll
@@ -103,72 +326,14 @@ __global__ __launch_bounds__(64) void qmv_kernel(const uint32_t* __restrict__ w,
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
-    for (int c = lane; c < chunks; c += 64) {
-        u32x4 wv[R];
-        float sv[R][PARTS], bv[R][PARTS];
-        const int g0 = (c * CPC) / GS;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int n = min(n0 + r, N - 1);      // rows past N compute garbage that is never stored
-            wv[r] = *reinterpret_cast<const u32x4*>(w + (size_t)n * row_words + 4 * (size_t)c);
-#pragma unroll
-            for (int p = 0; p < PARTS; ++p) {
-                const size_t gi = (size_t)n * G + g0 + p;
-                sv[r][p] = load_elem<DT>(scales, gi);
-                bv[r][p] = load_elem<DT>(biases, gi);
-            }
-        }
-
-        float qd[R][MT][PARTS];
-        float xs[MT][PARTS];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int p = 0; p < PARTS; ++p) {
-                xs[m][p] = 0.f;
-#pragma unroll
-                for (int r = 0; r < R; ++r) qd[r][m][p] = 0.f;
-            }
-
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = j / WPP;
-            float xv[MT][CPW];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < mcount) {
-                    load_x<DT, CPW>(x, (size_t)(m0 + m) * K + (size_t)c * CPC + j * CPW, xv[m]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < CPW; ++e) xv[m][e] = 0.f;
-                }
-                float t = 0.f;
-#pragma unroll
-                for (int e = 0; e < CPW; ++e) t += xv[m][e];
-                xs[m][p] += t;
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t word = j == 0 ? wv[r].x : j == 1 ? wv[r].y : j == 2 ? wv[r].z : wv[r].w;
-                float q[CPW];
-                unpack_word<BITS>(word, q);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    float t = qd[r][m][p];
-#pragma unroll
-                    for (int e = 0; e < CPW; ++e) t = fmaf(q[e], xv[m][e], t);
-                    qd[r][m][p] = t;
-                }
-            }
-        }
-
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int p = 0; p < PARTS; ++p)
-                    acc[r][m] = fmaf(sv[r][p], qd[r][m][p], fmaf(bv[r][p], xs[m][p], acc[r][m]));
+    int c = (int)((long)wave * chunks / KSPLIT) + lane;
+    // One chunk in flight per wave: the register budget goes to occupancy
+    // (6-7 waves per SIMD), which overlaps loads and arithmetic better on
+    // this kernel than a second register set at half the occupancy.
+    for (; c < c1; c += 64) {
+        S a;
+        qmv_load(a, w, scales, biases, x, c, n0, N, m0, mcount, K, G, row_words);
+        qmv_consume(a, acc);
     }
 
     float mine = 0.f;
@@ -179,25 +344,59 @@ __global__ __launch_bounds__(64) void qmv_kernel(const uint32_t* __restrict__ w,
             const float tot = wave_sum(acc[r][m]);
             if (lane == r * MT + m) mine = tot;
         }
+    if constexpr (KSPLIT > 1) {
+        __shared__ float part[KSPLIT][R * MT];
+        if (lane < R * MT) part[wave][lane] = mine;
+        __syncthreads();
+        if (wave != 0) return;
+        if (lane < R * MT) {
+            float t = part[0][lane];
+#pragma unroll
+            for (int k = 1; k < KSPLIT; ++k) t += part[k][lane];
+            mine = t;
+        }
+    }
     if (lane < R * MT) {
         const int r = lane / MT, m = lane % MT;
         if (n0 + r < N && m < mcount) store_elem<DT>(out, (size_t)(m0 + m) * N + n0 + r, mine);
     }
 }
 
-int qmv_mt_for(int M) { return M >= 4 ? 4 : (M == 3 ? 4 : (M == 2 ? 2 : 1)); }
+int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
+
+// Waves of one row tile that split its chunks: enough waves to give every CU
+// several, while each wave keeps at least 32 chunks.
+int qmv_ksplit_for(int M, int N, int K, int bits) {
+    if (qmv_mt_for(M) != 1) return 1;
+    const long waves = (long)((N + QMV_ROWS - 1) / QMV_ROWS);
+    const int chunks = K * bits / 128;
+    int ks = 1;
+    while (ks < 4 && waves * ks < 4096 && chunks / (2 * ks) >= 32) ks *= 2;
+    return ks;
+}
+
+template <int DT, int BITS, int GS, int MT, int KS>
+static void qmv_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                   int M, int N, int K, hipStream_t st) {
+    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, M, N,
+                       K);
+}
 
 template <int DT, int BITS, int GS>
 static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          int M, int N, int K, hipStream_t st) {
     const int mt = qmv_mt_for(M);
+    const int ks = qmv_ksplit_for(M, N, K, BITS);
     const dim3 grid((N + QMV_ROWS - 1) / QMV_ROWS, (M + mt - 1) / mt);
-    if (mt == 1)
-        hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, 1>), grid, dim3(64), 0, st, w, s, b, x, out, M, N, K);
-    else if (mt == 2)
-        hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, 2>), grid, dim3(64), 0, st, w, s, b, x, out, M, N, K);
-    else
-        hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, 4>), grid, dim3(64), 0, st, w, s, b, x, out, M, N, K);
+    if (mt == 1) {
+        if (ks == 4) qmv_go<DT, BITS, GS, 1, 4>(grid, w, s, b, x, out, M, N, K, st);
+        else if (ks == 2) qmv_go<DT, BITS, GS, 1, 2>(grid, w, s, b, x, out, M, N, K, st);
+        else qmv_go<DT, BITS, GS, 1, 1>(grid, w, s, b, x, out, M, N, K, st);
+    } else if (mt == 2) {
+        qmv_go<DT, BITS, GS, 2, 1>(grid, w, s, b, x, out, M, N, K, st);
+    } else {
+        qmv_go<DT, BITS, GS, 4, 1>(grid, w, s, b, x, out, M, N, K, st);
+    }
     return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ using qmx::QMM_BN;
 using qmx::QMM_KB;
 
 // Largest split count the dispatch policy picks by itself.
-constexpr int kPolicyMaxSplits = 4;
+constexpr int kPolicyMaxSplits = 16;
 // Default compute-unit count for planning without a device (MI355X).
 constexpr int kDefaultCUs = 256;
 

@@ -12,12 +12,13 @@ namespace qmx {
 constexpr int QMV_ROWS = 4;
 int qmv_mt_for(int M);
 
-// qmm_t geometry: 4 waves of 2 x 16 columns, 128-column K blocks.
-constexpr int QMM_WAVES = 4;
+// qmm_t geometry: 128-column K blocks of 4 MFMA k-steps; 8 waves = 4 along N
+// (2 x 16 columns each) x 2 halves that take alternate k-step pairs.
+constexpr int QMM_WAVES_N = 4;
 constexpr int QMM_NB = 2;
-constexpr int QMM_BN = QMM_WAVES * QMM_NB * 16;
+constexpr int QMM_BN = QMM_WAVES_N * QMM_NB * 16;
 constexpr int QMM_KB = 128;
-constexpr int QMM_THREADS = QMM_WAVES * 64;
+constexpr int QMM_THREADS = 2 * QMM_WAVES_N * 64;
 // 16-row x fragments per tile chosen for M (1, 2, 3, 4, 6 or 8) and the tile count.
 int qmm_mt_for(int M);
 int qmm_mtiles_for(int M);

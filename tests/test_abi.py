@@ -132,15 +132,15 @@ def test_block_validation():
     (1, 4096, 4096, BF16, "qmv", 1),
     (7, 4096, 4096, BF16, "qmv", 1),
     (16, 4096, 4096, F32, "qmv", 1),                 # float32 never takes the matrix cores
-    (16, 4096, 4096, BF16, "qmm_t_splitk", 4),       # 32 tiles on 256 CUs
+    (16, 4096, 4096, BF16, "qmm_t_splitk", 8),       # 32 tiles on 256 CUs
     (16, 4096, 256, BF16, "qmm_t", 1),               # K < 512 stays unsplit
-    (22, 2048, 2048, BF16, "qmm_t_splitk", 4),
-    (85, 2048, 10752, BF16, "qmm_t_splitk", 4),
-    (33, 4096, 14336, BF16, "qmm_t_splitk", 4),
-    (56, 5120, 17408, BF16, "qmm_t_splitk", 4),
+    (22, 2048, 2048, BF16, "qmm_t_splitk", 8),       # capped at K / 256 partitions
+    (85, 2048, 10752, BF16, "qmm_t_splitk", 16),
+    (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
+    (56, 5120, 17408, BF16, "qmm_t_splitk", 7),      # ceil(256 / 40 tiles)
     (512, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 4 M tiles x 32 N tiles = 128 tiles
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
-    (8, 4096, 4096, F16, "qmm_t_splitk", 4),
+    (8, 4096, 4096, F16, "qmm_t_splitk", 8),
     (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
 ])
 def test_plan_table(M, N, K, dtype, route, splits):
@@ -152,7 +152,7 @@ def test_plan_respects_split_limits():
         for N in (128, 1024, 4096):
             route, s = qmx.plan(16, N, K, 4, 64, BF16, 256)
             if route == "qmm_t_splitk":
-                assert 2 <= s <= 4 and K // s >= 256
+                assert 2 <= s <= 16 and K // s >= 256
     with pytest.raises(qmx.QmxError):
         qmx.plan(16, 4096, 96, 2, 32, F32, 256)      # qmv route cannot take 192-bit rows
     with pytest.raises(qmx.QmxError):

@@ -153,7 +153,7 @@ def test_qmm_config3_every_route(orc, KNM, route):
 def test_splitk_partials_match_partition_oracle(orc):
     """workspace[p] is the float32 partial of partition p: its K blocks are
     [floor(p*nkb/S), floor((p+1)*nkb/S)) of 128 columns."""
-    M, N, K, bits, gs, dt, S = 22, 256, 1664, 4, 64, qi.BF16, 3
+    M, N, K, bits, gs, dt, S = 22, 256, 1792, 4, 64, qi.BF16, 3
     say("splitk partials", M, N, K, S)
     c = qi.affine_case(M, N, K, bits, gs, dt, seed=1500)
     w, s, b, x = to_dev(c)
