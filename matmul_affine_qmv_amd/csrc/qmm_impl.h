@@ -1,41 +1,39 @@
 // qmm_impl.h -- the staged affine quantized x * W^T kernel for M >= 8 on the
 // gfx950 matrix cores.  Included once per code width by qmm_b{2,4,8}.hip.
 //
-// Method (page "mlx PR 4682"): transposed affine qmm with the next K step's
-// packed weights, scales/biases and activations prefetched into registers
-// while the current step is consumed from a threadgroup-memory buffer, the
-// prefetched step written into the other buffer, and one barrier per K step;
-// split-K writes float32 partials that a separate kernel sums.
+// Method (page "mlx PR 4682"): transposed affine qmm in which the next K
+// steps' packed weights, scales/biases and activations are fetched while the
+// current step is consumed from threadgroup memory, with one barrier per K
+// step; split-K writes float32 partials that a separate kernel sums.
 //
 // gfx950 mapping:
 // * A work-group of 8 waves owns an output tile of BM = 16*MT rows of x by
 //   BN = 128 columns of W and a range of 128-column K blocks (4 MFMA k-steps
 //   each).  Waves 0-3 each own 2 fragments of 16 columns and take k-steps
 //   0-1 of every block; waves 4-7 own the same columns and take k-steps 2-3.
-//   The two halves add their float32 tiles through LDS once at the end, so a
-//   CU runs two waves per SIMD without splitting K further across
-//   work-groups (which would cost HBM traffic for partials).
-// * Packed weights are used by exactly one wave, so they go straight from
-//   HBM into that wave's MFMA B-operand registers through a 4-deep register
-//   ring (three blocks in flight while one is consumed); they never touch LDS.
-// * x is shared by the 4 waves: it is prefetched two blocks ahead into
-//   registers, written to one of two LDS buffers in the k order the code
-//   expansion produces, and read back as MFMA A operands; the block's
-//   scales/biases are staged alongside in float32.  One barrier per K block.
+//   The two halves add their float32 tiles through LDS once at the end.
+// * Every operand of a K block (x rows, packed W rows, raw 16-bit scales and
+//   biases) is copied from HBM straight into an LDS stage by the global-to-LDS
+//   form of the load (no register staging, no conversion on the way in),
+//   through a ring of NS stages: NS - 1 blocks are in flight while one is
+//   consumed.  Each thread issues the same number of copies per stage, so a
+//   single wait on the per-wave memory counter plus one barrier per block
+//   makes a stage visible to the whole work-group.
+// * The copies land at consecutive LDS slots per lane; bank conflicts on the
+//   MFMA operand reads are avoided by choosing which global chunk each lane
+//   fetches (an XOR swizzle of the chunk index by the row), not by padding.
 // * Codes are expanded in registers right before the MFMA into exact 16-bit
-//   integers: one v_perm per pair of codes sets a magic exponent byte above
-//   two byte-aligned fields (0x43qq is the bf16 value 128 + q, 0x64qq the f16
-//   value 1024 + q).  The constant offset OFF*sum(x) this adds is removed in
-//   the group epilogue.  The codes come out in a fixed permutation of k; x
-//   is written to LDS in the same order, and since both MFMA operands see the
-//   same permutation the dot product is unchanged.
+//   integers in natural k order: fields are split into bytes, interleaved,
+//   and one v_perm per pair of codes sets a magic exponent byte above each
+//   (0x43qq is the bf16 value 128 + q, 0x64qq the f16 value 1024 + q).  The
+//   constant offset OFF*sum(x) this adds is removed in the group epilogue.
 // * MFMA v_mfma_f32_16x16x32_{bf16,f16}: A = x fragment (16 rows of M),
-//   B = W codes (16 columns of N).  A group of GS codes is GS/32 MFMA k-steps
+//   B = W codes (16 columns of N).  A group of GS codes is GS/32 k-steps
 //   accumulated into a fresh float32 tile; the same A fragments against an
 //   all-ones B give the group's row sums of x in a matching tile, and the
-//   epilogue adds scale * (tile) + (bias - OFF*scale) * (row sums) in float32.  Scale and bias
-//   never pass through a 16-bit format, so the output's only roundings are
-//   float32 accumulation and the final store.
+//   epilogue adds scale * (tile) + (bias - OFF*scale) * (row sums) in
+//   float32.  Scale and bias are used exactly as stored, so the output's
+//   only roundings are float32 accumulation and the final store.
 // * Work-groups are numbered so that the ones sharing a K range (and so the
 //   same x slice) are dispatched to the same XCD and share its L2.
 #pragma once
@@ -48,27 +46,43 @@ namespace qmx {
 template <int DT, int BITS, int GS, int MT>
 struct QmmCfg {
     static constexpr int BM = 16 * MT;
-    static constexpr int GPB = QMM_KB / GS;                  // groups per K block
-    static constexpr int S = GS / 4;                         // codes per lane group per group
-    static constexpr int KS = GS / 32;                       // MFMA k-steps per group
-    static constexpr int XP = QMM_KB + 8;                    // x LDS row pitch (elements)
-    static constexpr int WROW = QMM_KB * BITS / 32;          // words per W row per block
-    static constexpr int WPS = BITS == 8 ? 2 : 1;            // words a lane loads per k-step
-    static constexpr int WRING = 4;                          // register ring depth for W
-    static constexpr int XPR = QMM_KB / 8;                   // 16-byte x pieces per row per block
-    static constexpr int XPT = (MT * 16 * XPR + QMM_THREADS - 1) / QMM_THREADS;  // pieces per thread
-    static constexpr int XROWS = XPT * QMM_THREADS / XPR;    // x rows held in LDS (>= BM)
-    static constexpr int X_BYTES = XROWS * XP * 2;
-    static constexpr int SB_BYTES = 2 * GPB * QMM_BN * 4;
-    static constexpr int BUF_BYTES = X_BYTES + SB_BYTES;
-    static constexpr int SB_SLICES = QMM_THREADS / QMM_BN;   // thread slices over the groups of a block
-    static constexpr float OFF = (DT == DT_F16) ? 1024.f : (BITS == 8 ? 0.f : 128.f);
+    static constexpr int GPB = QMM_KB / GS;                   // groups per K block
+    static constexpr int KS = GS / 32;                        // MFMA k-steps per group
+    // x: each wave-wide 16-byte copy fills 1 KB = 4 rows of 128 16-bit values.
+    static constexpr int XPT = (BM + 31) / 32;                // x copies per thread per block
+    static constexpr int XROWS = 32 * XPT;
+    static constexpr int X_BYTES = XROWS * 256;
+    // W: 16*BITS bytes per row per block.  2-bit rows are copied 4 bytes per
+    // lane (two copies per thread), wider ones 16 bytes per lane.
+    static constexpr int W_ROW = 16 * BITS;
+    static constexpr int W_BYTES = QMM_BN * W_ROW;
+    static constexpr int WPT = BITS == 4 ? 1 : 2;             // W copies per thread per block
+    // scales then biases, one 16-bit value per lane (zero-extended to 4 bytes in LDS)
+    static constexpr int SB_VALUES = 2 * QMM_BN * GPB;
+    static constexpr int SBPT = (SB_VALUES + QMM_THREADS - 1) / QMM_THREADS;
+    static constexpr int SB_BYTES = SBPT * QMM_THREADS * 4;
+    static constexpr int STAGE = X_BYTES + W_BYTES + SB_BYTES;
+    static constexpr int NS = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
+    static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
+    static constexpr bool CVT8 = DT == DT_BF16 && BITS == 8;  // 128 + q is not exact in bf16
+    static constexpr float OFF = CVT8 ? 0.f : (DT == DT_F16 ? 1024.f : 128.f);
     static constexpr int RED_BYTES = QMM_WAVES_N * MT * QMM_NB * 4 * 64 * 4;
-    static_assert(BUF_BYTES % 16 == 0, "buffer alignment");
-    static_assert(2 * BUF_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(RED_BYTES <= 2 * BUF_BYTES, "end reduction reuses the LDS buffers");
-    static_assert(GPB <= SB_SLICES, "one scale/bias slice per group");
+    static_assert(NS >= 3, "at least two stages in flight");
+    static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
+    static_assert(LPS * (NS - 2) < 64, "memory counter range");
+    static_assert(STAGE % 1024 == 0 && X_BYTES % 1024 == 0, "stage alignment");
 };
+
+// 8-value chunk of the 128-column block that lane group g feeds at k-step s.
+// Each step's 32 values lie inside one group of GS.  2-bit codes with GS >= 64
+// pair steps so that a lane's two steps are the two halves of one W word.
+template <int BITS, int GS>
+__device__ __forceinline__ constexpr int kchunk(int s, int g) {
+    if constexpr (BITS == 2 && GS >= 64)
+        return 8 * (s / 2) + 2 * g + (s % 2);
+    else
+        return 4 * s + g;
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -80,84 +94,77 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// 8 codes of one unit as 16-bit MFMA operands (exact integers).  The word
-// is split into byte-aligned fields and one v_perm per pair puts two field
-// bytes under the magic exponent byte: 0x43qq is the bf16 value 128 + q and
-// 0x64qq the f16 value 1024 + q.  Element orders of the 8 operand slots:
-//   4-bit: 0,2,4,6,1,3,5,7   (low nibbles, then high nibbles, of one word)
-//   2-bit: 0,4,1,5,2,6,3,7   (fields t of the unit's two bytes)
-//   8-bit: 0..7              (bytes of two words; bf16 converts, since 128 + q
-//                             would overflow the bf16 mantissa for q >= 128)
-__device__ constexpr uint32_t perm_sel(int i, int j) {   // bytes i, j of the field word under the magic byte
+// v_perm selector: byte i of the low source, then the magic byte (byte 0 of
+// the high source), then byte j, then the magic byte again.
+__device__ constexpr uint32_t perm_sel(int i, int j) {
     return (uint32_t)i | (4u << 8) | ((uint32_t)j << 16) | (4u << 24);
 }
 
-template <int DT, int BITS>
-__device__ __forceinline__ u32x4 unpack_unit(uint32_t w0, uint32_t w1) {
+// Eight byte-held codes (bytes of e = c0 c1 c4 c5 and f = c2 c3 c6 c7) as
+// four pairs of 16-bit MFMA operands in natural order.
+template <int DT>
+__device__ __forceinline__ u32x4 magic_pairs(uint32_t e, uint32_t f) {
     constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
-    u32x4 r;
-    if constexpr (BITS == 4) {
-        const uint32_t lo = w0 & 0x0f0f0f0fu, hi = (w0 >> 4) & 0x0f0f0f0fu;
-        r.x = __builtin_amdgcn_perm(MB, lo, perm_sel(0, 1));
-        r.y = __builtin_amdgcn_perm(MB, lo, perm_sel(2, 3));
-        r.z = __builtin_amdgcn_perm(MB, hi, perm_sel(0, 1));
-        r.w = __builtin_amdgcn_perm(MB, hi, perm_sel(2, 3));
-    } else if constexpr (BITS == 2) {
-        // w0 holds the unit in its low 16 bits: byte 0 = codes 0-3, byte 1 = codes 4-7
-        r.x = __builtin_amdgcn_perm(MB, w0 & 0x0303u, perm_sel(0, 1));
-        r.y = __builtin_amdgcn_perm(MB, (w0 >> 2) & 0x0303u, perm_sel(0, 1));
-        r.z = __builtin_amdgcn_perm(MB, (w0 >> 4) & 0x0303u, perm_sel(0, 1));
-        r.w = __builtin_amdgcn_perm(MB, (w0 >> 6) & 0x0303u, perm_sel(0, 1));
-    } else if constexpr (DT == DT_F16) {
-        r.x = __builtin_amdgcn_perm(MB, w0, perm_sel(0, 1));
-        r.y = __builtin_amdgcn_perm(MB, w0, perm_sel(2, 3));
-        r.z = __builtin_amdgcn_perm(MB, w1, perm_sel(0, 1));
-        r.w = __builtin_amdgcn_perm(MB, w1, perm_sel(2, 3));
+    return u32x4{__builtin_amdgcn_perm(MB, e, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, f, perm_sel(0, 1)),
+                 __builtin_amdgcn_perm(MB, e, perm_sel(2, 3)), __builtin_amdgcn_perm(MB, f, perm_sel(2, 3))};
+}
+
+// 8 consecutive 4-bit codes of one word (code i at bits 4i).
+template <int DT>
+__device__ __forceinline__ u32x4 expand4(uint32_t w) {
+    const uint32_t lo = w & 0x0f0f0f0fu;          // c0 c2 c4 c6
+    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;   // c1 c3 c5 c7
+    const uint32_t c0123 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    const uint32_t c4567 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
+    return u32x4{__builtin_amdgcn_perm(MB, c0123, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c0123, perm_sel(2, 3)),
+                 __builtin_amdgcn_perm(MB, c4567, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c4567, perm_sel(2, 3))};
+}
+
+// 8 consecutive 2-bit codes held in the low 16 bits of h (code i at bits 2i).
+template <int DT>
+__device__ __forceinline__ u32x4 expand2(uint32_t h) {
+    const uint32_t a = h & 0x0303u, b = (h >> 2) & 0x0303u;          // c0 c4, c1 c5
+    const uint32_t c = (h >> 4) & 0x0303u, d = (h >> 6) & 0x0303u;   // c2 c6, c3 c7
+    return magic_pairs<DT>(__builtin_amdgcn_perm(b, a, 0x05010400u), __builtin_amdgcn_perm(d, c, 0x05010400u));
+}
+
+// 8 consecutive 8-bit codes of two words.
+template <int DT>
+__device__ __forceinline__ u32x4 expand8(uint32_t w0, uint32_t w1) {
+    if constexpr (DT == DT_F16) {
+        constexpr uint32_t MB = 0x64646464u;
+        return u32x4{__builtin_amdgcn_perm(MB, w0, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w0, perm_sel(2, 3)),
+                     __builtin_amdgcn_perm(MB, w1, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w1, perm_sel(2, 3))};
     } else {
-        // bf16 holds every integer up to 256 exactly: convert, keep the upper half.
+        // bf16 holds every integer up to 256 exactly: convert, keep the upper halves.
         auto pair = [](uint32_t a, uint32_t b) {
             return __builtin_amdgcn_perm(__float_as_uint((float)b), __float_as_uint((float)a), 0x07060302u);
         };
-        r.x = pair(w0 & 0xffu, (w0 >> 8) & 0xffu);
-        r.y = pair((w0 >> 16) & 0xffu, w0 >> 24);
-        r.z = pair(w1 & 0xffu, (w1 >> 8) & 0xffu);
-        r.w = pair((w1 >> 16) & 0xffu, w1 >> 24);
-    }
-    return r;
-}
-
-// Eight consecutive 16-bit x values (d = x0x1, x2x3, x4x5, x6x7) in the
-// slot order unpack_unit uses for BITS.
-template <int BITS>
-__device__ __forceinline__ u32x4 permute_x(u32x4 d) {
-    if constexpr (BITS == 8) {
-        return d;
-    } else if constexpr (BITS == 4) {
-        // (x0,x2) (x4,x6) (x1,x3) (x5,x7)
-        return u32x4{__builtin_amdgcn_perm(d.y, d.x, 0x05040100u), __builtin_amdgcn_perm(d.w, d.z, 0x05040100u),
-                     __builtin_amdgcn_perm(d.y, d.x, 0x07060302u), __builtin_amdgcn_perm(d.w, d.z, 0x07060302u)};
-    } else {
-        // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-        return u32x4{__builtin_amdgcn_perm(d.z, d.x, 0x05040100u), __builtin_amdgcn_perm(d.z, d.x, 0x07060302u),
-                     __builtin_amdgcn_perm(d.w, d.y, 0x05040100u), __builtin_amdgcn_perm(d.w, d.y, 0x07060302u)};
+        return u32x4{pair(w0 & 0xffu, (w0 >> 8) & 0xffu), pair((w0 >> 16) & 0xffu, w0 >> 24),
+                     pair(w1 & 0xffu, (w1 >> 8) & 0xffu), pair((w1 >> 16) & 0xffu, w1 >> 24)};
     }
 }
 
-// WPL consecutive words at p (WPL = 1, 2, 4 or 8; 16-byte aligned for 4 and 8).
-template <int WPL>
-__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&v)[WPL]) {
-    if constexpr (WPL == 1) {
-        v[0] = p[0];
-    } else if constexpr (WPL == 2) {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-        v[0] = a.x; v[1] = a.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < WPL / 4; ++i) {
-            const u32x4 a = reinterpret_cast<const u32x4*>(p)[i];
-            v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
-        }
-    }
+// Copy BYTES (2, 4 or 16) per lane from g into LDS at the wave-uniform address
+// l: lane i's data lands at l + 16 * i for 16-byte copies and at l + 4 * i
+// (zero-extended) for the smaller ones.
+template <int BYTES>
+__device__ __forceinline__ void dma(const void* g, unsigned char* l) {
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_global_load_lds(g, reinterpret_cast<void*>(l), 16, 0, 0);
+    else if constexpr (BYTES == 4)
+        __builtin_amdgcn_global_load_lds(g, reinterpret_cast<void*>(l), 4, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(g, reinterpret_cast<void*>(l), 2, 0, 0);
+}
+
+// Wait until at most N of this wave's copies are in flight and its LDS reads
+// are done, then meet the other waves.  The memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int DT, int BITS, int GS, int MT, bool SPLIT>
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
     using C = QmmCfg<DT, BITS, GS, MT>;
     constexpr int NB = QMM_NB;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::BUF_BYTES];
+    constexpr int NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * C::STAGE];
 
     // Hardware block h runs on XCD h % 8; give each XCD a contiguous range of tiles.
     const int h = blockIdx.x;
@@ -185,79 +193,68 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const int G = K / GS;
     const size_t row_words = (size_t)K * BITS / 32;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & (QMM_WAVES_N - 1);   // column slice of this wave
     const int wk = wave / QMM_WAVES_N;          // k-step pair of this wave: steps 2wk, 2wk+1 of each block
     const int lrow = lane & 15, lgrp = lane >> 4;
 
-    // ---- x (+ scales/biases) ring: 2 register slots -> 2 LDS buffers.
-    // Every prefetch load is unconditional, with the block index and the row
-    // and column indices clamped into range: rows of x past M and columns
-    // past N then only feed outputs that are never stored.  Loaded values are
-    // left untouched until they are written to LDS two blocks later, so the
-    // compiler never has to wait on a load it has just issued.
-    u32x4 xr[2][C::XPT];
-    uint32_t sr[2], br[2];
-    const int sb_col = tid % QMM_BN;
-    const int sb_g = tid / QMM_BN;
-    const bool sb_active = sb_g < C::GPB;
-    const int sb_n = min(n0 + sb_col, N - 1);
-    const int sb_gl = min(sb_g, C::GPB - 1);   // in-range group for inactive slices
+    // ---- per-thread sources of the stage copies at block 0 (block kb adds a fixed stride)
+    // x: copy i of this thread fills row r = 4*(8i + wave) + lane/16 of the stage at
+    // 16-byte slot lane%16, with chunk slot ^ (r & 15) of that row of x.
+    const uint16_t* xsrc[C::XPT];
+#pragma unroll
+    for (int i = 0; i < C::XPT; ++i) {
+        const int r = 4 * (8 * i + wave) + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        xsrc[i] = static_cast<const uint16_t*>(x) + (size_t)min(m0 + r, M - 1) * K + 8 * c;
+    }
+    // W: tile rows R in 16-byte chunks (4-byte words for 2-bit codes); the chunk a
+    // slot holds is its index XOR a few bits of R, so B-operand reads spread over banks.
+    const uint32_t* wsrc[C::WPT];
+#pragma unroll
+    for (int j = 0; j < C::WPT; ++j) {
+        int R, q;
+        if constexpr (BITS == 4) {
+            R = 16 * wave + (lane >> 2);
+            q = 4 * ((lane & 3) ^ ((R >> 2) & 3));
+        } else if constexpr (BITS == 8) {
+            R = 8 * (8 * j + wave) + (lane >> 3);
+            q = 4 * ((lane & 7) ^ ((R >> 1) & 7));
+        } else {
+            R = 8 * (8 * j + wave) + (lane >> 3);
+            q = (lane & 7) ^ ((R >> 3) & 7);
+        }
+        wsrc[j] = w + (size_t)min(n0 + R, N - 1) * row_words + q;
+    }
+    // scales/biases: value v = 512j + tid (modulo the value count) is the scale (then
+    // the bias) of column (v % (BN*GPB)) / GPB, group v % GPB, and lands at LDS word v.
+    const uint16_t* sbsrc[C::SBPT];
+#pragma unroll
+    for (int j = 0; j < C::SBPT; ++j) {
+        const int v = (QMM_THREADS * j + tid) % C::SB_VALUES;
+        const int which = v / (QMM_BN * C::GPB);
+        const int rem = v % (QMM_BN * C::GPB);
+        const int col = rem / C::GPB, g = rem % C::GPB;
+        sbsrc[j] = static_cast<const uint16_t*>(which ? biases : scales) + (size_t)min(n0 + col, N - 1) * G + g;
+    }
 
-    auto x_gload = [&](int kb_req, int slot) {
-        const int kb = min(kb_req, kb1 - 1);
-        const int k0 = kb * QMM_KB;
+    auto stage_load = [&](int kb, int buf) {
+        unsigned char* X = smem + buf * C::STAGE;
+        unsigned char* Wl = X + C::X_BYTES;
+        unsigned char* SB = Wl + C::W_BYTES;
 #pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int p = tid + QMM_THREADS * i;              // piece p: row p / XPR, unit p % XPR
-            const int m = min(m0 + p / C::XPR, M - 1);
-            xr[slot][i] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + (size_t)m * K + k0 +
-                                                          8 * (p % C::XPR));
-        }
-        const size_t gi = (size_t)sb_n * G + (size_t)kb * C::GPB + sb_gl;
-        sr[slot] = static_cast<const uint16_t*>(scales)[gi];
-        br[slot] = static_cast<const uint16_t*>(biases)[gi];
-    };
-
-    auto x_lstore = [&](int slot, int buf) {
-        unsigned char* base = smem + buf * C::BUF_BYTES;
-        uint16_t* xl = reinterpret_cast<uint16_t*>(base);
-        float* sbl = reinterpret_cast<float*>(base + C::X_BYTES);
+        for (int i = 0; i < C::XPT; ++i) dma<16>(xsrc[i] + (size_t)kb * QMM_KB, X + (8 * i + wave) * 1024);
 #pragma unroll
-        for (int i = 0; i < C::XPT; ++i) {
-            const int p = tid + QMM_THREADS * i;
-            *reinterpret_cast<u32x4*>(xl + (p / C::XPR) * C::XP + 8 * (p % C::XPR)) = permute_x<BITS>(xr[slot][i]);
+        for (int j = 0; j < C::WPT; ++j) {
+            if constexpr (BITS == 2)
+                dma<4>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 256);
+            else
+                dma<16>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 1024);
         }
-        if (sb_active) {
-            const float sv = DT == DT_F16 ? f16_bits_to_f32(sr[slot]) : bf16_bits_to_f32(sr[slot]);
-            const float bv = DT == DT_F16 ? f16_bits_to_f32(br[slot]) : bf16_bits_to_f32(br[slot]);
-            sbl[sb_g * QMM_BN + sb_col] = sv;
-            sbl[(C::GPB + sb_g) * QMM_BN + sb_col] = fmaf(-C::OFF, sv, bv);
-        }
-    };
-
-    // ---- W ring: WRING register slots of this wave's B-operand words (2 k-steps)
-    // code offset (within the block) of this lane's unit in k-step s
-    auto unit_code = [&](int s) { return (s / C::KS) * GS + lgrp * C::S + 8 * (s % C::KS); };
-    uint32_t wr[C::WRING][NB][2][C::WPS];
-    auto w_gload = [&](int kb_req, int slot) {
-        const int kb = min(kb_req, kb1 - 1);
 #pragma unroll
-        for (int nf = 0; nf < NB; ++nf) {
-            const int n = min(n0 + wn * (NB * 16) + nf * 16 + lrow, N - 1);
-            const uint32_t* row = w + (size_t)n * row_words + (size_t)kb * C::WROW;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int word = unit_code(2 * wk + st) * BITS / 32;
-                if constexpr (C::WPS == 2) {
-                    const u32x2 v = *reinterpret_cast<const u32x2*>(row + word);
-                    wr[slot][nf][st][0] = v.x;
-                    wr[slot][nf][st][1] = v.y;
-                } else {
-                    wr[slot][nf][st][0] = row[word];
-                }
-            }
-        }
+        for (int j = 0; j < C::SBPT; ++j)
+            dma<2>(sbsrc[j] + (size_t)kb * C::GPB, SB + (QMM_THREADS * j + 64 * wave) * 4);
     };
 
     f32x4 run[MT][NB];
@@ -269,26 +266,38 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     constexpr uint32_t ONE2 = DT == DT_F16 ? 0x3c003c00u : 0x3f803f80u;
     const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
 
-    auto compute = [&](int buf, int wslot) {
-        const unsigned char* base = smem + buf * C::BUF_BYTES;
-        const uint16_t* xl = reinterpret_cast<const uint16_t*>(base);
-        const float* sbl = reinterpret_cast<const float*>(base + C::X_BYTES);
-        // expand this wave's two k-steps of codes once
+    auto compute = [&](int buf) {
+        const unsigned char* X = smem + buf * C::STAGE;
+        const unsigned char* Wl = X + C::X_BYTES;
+        const uint32_t* SB = reinterpret_cast<const uint32_t*>(Wl + C::W_BYTES);
+        // expand this wave's two k-steps of codes
         u32x4 bf[2][NB];
-        int off[2];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int c = unit_code(2 * wk + st);
-            off[st] = c;
+        for (int nf = 0; nf < NB; ++nf) {
+            const int R = wn * (NB * 16) + nf * 16 + lrow;
+            if constexpr (BITS == 2 && GS >= 64) {
+                const int c = kchunk<BITS, GS>(2 * wk, lgrp);   // both steps share word c / 2
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(Wl + R * C::W_ROW +
+                                                                         (((c >> 1) ^ ((R >> 3) & 7)) << 2));
+                bf[0][nf] = expand2<DT>(word & 0xffffu);
+                bf[1][nf] = expand2<DT>(word >> 16);
+            } else {
 #pragma unroll
-            for (int nf = 0; nf < NB; ++nf) {
-                const uint32_t* bw = wr[wslot][nf][st];
-                if constexpr (BITS == 4) {
-                    bf[st][nf] = unpack_unit<DT, 4>(bw[0], 0u);
-                } else if constexpr (BITS == 8) {
-                    bf[st][nf] = unpack_unit<DT, 8>(bw[0], bw[1]);
-                } else {
-                    bf[st][nf] = unpack_unit<DT, 2>((bw[0] >> (16 * ((c >> 3) & 1))) & 0xffffu, 0u);
+                for (int st = 0; st < 2; ++st) {
+                    const int c = kchunk<BITS, GS>(2 * wk + st, lgrp);
+                    if constexpr (BITS == 4) {
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(
+                            Wl + R * C::W_ROW + (((c >> 2) ^ ((R >> 2) & 3)) << 4) + 4 * (c & 3));
+                        bf[st][nf] = expand4<DT>(word);
+                    } else if constexpr (BITS == 8) {
+                        const u32x2 wv = *reinterpret_cast<const u32x2*>(
+                            Wl + R * C::W_ROW + (((c >> 1) ^ ((R >> 1) & 7)) << 4) + 8 * (c & 1));
+                        bf[st][nf] = expand8<DT>(wv.x, wv.y);
+                    } else {
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(Wl + R * C::W_ROW +
+                                                                                 (((c >> 1) ^ ((R >> 3) & 7)) << 2));
+                        bf[st][nf] = expand2<DT>((word >> (16 * (c & 1))) & 0xffffu);
+                    }
                 }
             }
         }
@@ -297,20 +306,26 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         float sv[NG][NB], bv[NG][NB];
 #pragma unroll
         for (int gp = 0; gp < NG; ++gp) {
-            const int g = (2 * wk + gp) / C::KS;
+            const int g = (32 * (2 * wk + gp)) / GS;
 #pragma unroll
             for (int nf = 0; nf < NB; ++nf) {
                 const int col = wn * (NB * 16) + nf * 16 + lrow;
-                sv[gp][nf] = sbl[g * QMM_BN + col];
-                bv[gp][nf] = sbl[(C::GPB + g) * QMM_BN + col];
+                const uint32_t sr = SB[col * C::GPB + g];
+                const uint32_t br = SB[QMM_BN * C::GPB + col * C::GPB + g];
+                const float s = DT == DT_F16 ? f16_bits_to_f32(sr) : bf16_bits_to_f32(sr);
+                const float b = DT == DT_F16 ? f16_bits_to_f32(br) : bf16_bits_to_f32(br);
+                sv[gp][nf] = s;
+                bv[gp][nf] = fmaf(-C::OFF, s, b);
             }
         }
+        const int c0 = kchunk<BITS, GS>(2 * wk, lgrp), c1 = kchunk<BITS, GS>(2 * wk + 1, lgrp);
         // one 16-row fragment of x at a time keeps one row of group tiles live; the
         // group's row sums of x come from one more MFMA against ones
 #pragma unroll
         for (int mf = 0; mf < MT; ++mf) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xl + (mf * 16 + lrow) * C::XP + off[0]);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xl + (mf * 16 + lrow) * C::XP + off[1]);
+            const int r = mf * 16 + lrow;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c0 ^ (r & 15)) << 4));
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c1 ^ (r & 15)) << 4));
 #pragma unroll
             for (int gp = 0; gp < NG; ++gp) {
                 f32x4 gacc[NB];
@@ -339,30 +354,26 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         }
     };
 
-    if (nk > 0) {
-        x_gload(kb0, 0);
-        x_gload(kb0 + 1, 1);
+    // Ring of NS stages: block i lives in stage i % NS.  Before consuming block i
+    // every thread waits for its own copies of block i (the copies of the NS - 2
+    // later blocks may still be in flight; near the end, where fewer were issued,
+    // it waits for all), and the barrier publishes them.  The copies of block
+    // i + NS - 1 then go into the stage that block i - 1 used, which every wave
+    // finished reading before the barrier.
 #pragma unroll
-        for (int i = 0; i < C::WRING; ++i) w_gload(kb0 + i, i);
-        x_lstore(0, 0);
-        x_gload(kb0 + 2, 0);
-        __syncthreads();
-        // Block i: compute from LDS buffer i%2 and W slot i%4; then stage x(i+1)
-        // into the other buffer and request x(i+3) and W(i+4) into the freed
-        // slots.  Past the last block the requests repeat the last block and
-        // the staged data is never read.
-        for (int base = 0; base < nk; base += C::WRING) {
-#pragma unroll
-            for (int j = 0; j < C::WRING; ++j) {
-                const int i = base + j;
-                if (i < nk) compute(j & 1, j);
-                x_lstore((j + 1) & 1, (j + 1) & 1);
-                x_gload(kb0 + i + 3, (j + 1) & 1);
-                w_gload(kb0 + i + C::WRING, j);
-                __syncthreads();
-            }
-        }
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nk) stage_load(kb0 + p, p);
+    int buf = 0;
+    for (int i = 0; i < nk; ++i) {
+        if (i + NS - 2 < nk)
+            stage_barrier<C::LPS * (NS - 2)>();
+        else
+            stage_barrier<0>();
+        if (i + NS - 1 < nk) stage_load(kb0 + i + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+        compute(buf);
+        buf = buf == NS - 1 ? 0 : buf + 1;
     }
+    stage_barrier<0>();
 
     // add the second half's tiles to the first half's, then store
     float* red = reinterpret_cast<float*>(smem);
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
                 for (int v = 0; v < 4; ++v)
                     red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane] = run[mf][nf][v];
     }
-    __syncthreads();
+    stage_barrier<0>();
     if (wk == 1) return;
 #pragma unroll
     for (int mf = 0; mf < MT; ++mf)

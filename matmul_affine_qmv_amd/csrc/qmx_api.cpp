@@ -107,7 +107,8 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     *route = QMX_ROUTE_QMM_T;
     *splits = 1;
     if (K < 4 * QMM_KB || tiles >= num_cus || tiles == 0) return QMX_OK;
-    long long s = (num_cus + tiles - 1) / tiles;
+    // as many partitions as keep every work-group of the launch resident at once
+    long long s = num_cus / tiles;
     const int cap = max_splits_for(K) < kPolicyMaxSplits ? max_splits_for(K) : kPolicyMaxSplits;
     if (s > cap) s = cap;
     if (s >= 2) {

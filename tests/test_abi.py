@@ -137,7 +137,7 @@ def test_block_validation():
     (22, 2048, 2048, BF16, "qmm_t_splitk", 8),       # capped at K / 256 partitions
     (85, 2048, 10752, BF16, "qmm_t_splitk", 16),
     (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
-    (56, 5120, 17408, BF16, "qmm_t_splitk", 7),      # ceil(256 / 40 tiles)
+    (56, 5120, 17408, BF16, "qmm_t_splitk", 6),      # floor(256 / 40 tiles)
     (512, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 4 M tiles x 32 N tiles = 128 tiles
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
     (8, 4096, 4096, F16, "qmm_t_splitk", 8),
