@@ -192,11 +192,25 @@ def per_call_us(c, sets, idx, reps):
     return 1000.0 * ms / (reps * len(sets))
 
 
-def roofline_for(c, us):
-    b, f = alg_bytes(c), flops(c)
+def per_kernel_us(fn, sets, idx, reps):
+    """Average µs per launch of one kernel: a graph launches it once per rotating
+    set; the graph is replayed `reps` times between two HIP events on the
+    stream the kernels run on."""
+    g = capture(lambda: [fn(s[idx]) for s in sets])
+    g.replay()
+    _, ms = time_graphs([g], reps)
+    return 1000.0 * ms / (reps * len(sets))
+
+
+def roofline_for(c, us, nbytes=None, nflops=None, matrix=None):
+    """Roofline of one launch: HBM-bound unless the bf16/f16 MFMA time at the
+    published peak exceeds the HBM time at the published peak."""
+    b = alg_bytes(c) if nbytes is None else nbytes
+    f = flops(c) if nflops is None else nflops
+    if matrix is None:
+        matrix = c["kind"] == "affine" and c["route"] == "qmm" and c["M"] >= 8 and c["dtype"] != F32
     t_hbm = b / (HBM_PEAK_GBS * 1e9)
-    t_mfma = f / (MFMA_BF16_TFLOPS * 1e12) if (c["kind"] == "affine" and c["route"] == "qmm"
-                                                and c["M"] >= 8 and c["dtype"] != F32) else 0.0
+    t_mfma = f / (MFMA_BF16_TFLOPS * 1e12) if matrix else 0.0
     s = us * 1e-6
     if t_mfma > t_hbm:
         ach = f / s / 1e12
@@ -204,6 +218,45 @@ def roofline_for(c, us):
                 "frac": ach / MFMA_BF16_TFLOPS}
     ach = b / s / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS}
+
+
+def kernels_of(c, route, splits):
+    """The kernels one call launches, each as (label, launcher over an input set,
+    algorithmic bytes per launch, flops per launch, on the matrix cores)."""
+    import matmul_affine_qmv_amd as qmx
+    if c["kind"] != "affine" or route != "qmm_t_splitk":
+        label = {"qmv": "qmv_kernel", "qmm_t": "qmm_t_kernel", "q8_0": "q8_0_kernel",
+                 "q4_k": "q4_k_kernel"}[route if c["kind"] == "affine" else c["kind"]]
+        return [(label, lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), route == "qmm_t")]
+    M, N, K, e = c["M"], c["N"], c["K"], 2
+    parts = splits * M * N * 4
+    inputs = alg_bytes(c) - M * N * e
+    kw = dict(bits=c["bits"], group_size=c["gs"], splits=splits)
+    return [
+        ("qmm_t_kernel (split-K partials)",
+         lambda d: qmx.qmm_t_partials(d["w"], d["scales"], d["biases"], d["x"], workspace=d["ws"], **kw),
+         inputs + parts, flops(c), True),
+        ("splitk_accum_kernel", lambda d: qmx.splitk_accumulate(d["ws"], d["out"], splits), parts + M * N * e,
+         0, False),
+    ]
+
+
+def stored_traffic(call, label):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel, if a
+    summary under profiles/ matches the current kernel sources; else None."""
+    import glob
+
+    from matmul_affine_qmv_amd import traffic
+    digest = traffic.source_digest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json"))):
+        try:
+            with open(path) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if t.get("call") == call and t.get("kernel_label") == label and t.get("source_sha256") == digest:
+            return t["traffic_bytes_per_launch"], os.path.relpath(path, ROOT)
+    return None, None
 
 
 # ---------------------------------------------------------------- oracle baseline
@@ -312,22 +365,26 @@ def main(argv=None):
     step_flops = sum(flops(c) for c in calls)
     value = args.steps * step_bytes / wall / 1e9
 
-    details = []
+    details, kernels = [], []
     for i, c in enumerate(calls):
         us = per_call_us(c, sets, i, args.reps)
-        route = c["route"]
+        route, splits = c["route"], 1
         if c["kind"] == "affine" and route == "qmm":
-            r, s = qmx.plan(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"])
-            route = r if r != "qmm_t_splitk" else f"qmm_t_splitk{s}"
-        rf = roofline_for(c, us)
-        details.append({"call": call_name(c), "route": route, "us": us, "alg_bytes": alg_bytes(c),
+            route, splits = qmx.plan(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"])
+        shown = route if route != "qmm_t_splitk" else f"qmm_t_splitk{splits}"
+        details.append({"call": call_name(c), "route": shown, "us": us, "alg_bytes": alg_bytes(c),
                         "gbs": alg_bytes(c) / us / 1e3, "hbm_frac": alg_bytes(c) / us / 1e3 / HBM_PEAK_GBS,
-                        "tflops": flops(c) / us / 1e6, "roofline": rf})
-    dom_i = max(range(len(calls)), key=lambda i: details[i]["us"])
-    dom = details[dom_i]
+                        "tflops": flops(c) / us / 1e6, "roofline": roofline_for(c, us)})
+        for label, fn, kb, kf, matrix in kernels_of(c, route if c["kind"] == "affine" else c["kind"], splits):
+            kus = per_kernel_us(fn, sets, i, args.reps)
+            kernels.append({"call": call_name(c), "kernel": label, "us": kus, "alg_bytes": kb, "flops": kf,
+                            "roofline": roofline_for(c, kus, kb, kf, matrix)})
+    dom = max(kernels, key=lambda k: k["us"])
     roof = dict(dom["roofline"])
-    roof.update({"kernel_call": dom["call"], "route": dom["route"], "us_per_launch": dom["us"],
-                 "alg_bytes_per_launch": dom["alg_bytes"], "traffic": None})
+    traffic, traffic_src = stored_traffic(dom["call"], dom["kernel"])
+    roof.update({"kernel": dom["kernel"], "call": dom["call"], "us_per_launch": dom["us"],
+                 "alg_bytes_per_launch": dom["alg_bytes"], "flops_per_launch": dom["flops"],
+                 "traffic": traffic, "traffic_source": traffic_src})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -353,12 +410,13 @@ def main(argv=None):
         "us_per_call": {d["call"]: round(d["us"], 3) for d in details},
         "hbm_frac_per_call": {d["call"]: round(d["hbm_frac"], 4) for d in details},
         "routes": {d["call"]: d["route"] for d in details},
+        "us_per_kernel": {f"{k['call']}:{k['kernel']}": round(k["us"], 3) for k in kernels},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     if args.detail_out:
         with open(args.detail_out, "w") as f:
-            json.dump({"line": line, "details": details}, f, indent=1)
+            json.dump({"line": line, "details": details, "kernels": kernels}, f, indent=1)
     print(json.dumps(line), flush=True)
     return 0
 

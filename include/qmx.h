@@ -127,6 +127,26 @@ int qmx_qmm_t_splitk(const uint32_t* w_packed, const void* scales, const void* b
                      int dtype, int splits, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* qmx_qmm_t_partials -- the first kernel of qmx_qmm_t_splitk on its own:
+ * writes partition p's float32 sums into workspace[p][m][n] for
+ * p = 0..splits-1 (the split-K partial kernel of page "mlx PR 4682") and
+ * touches nothing else.  Arguments, partitions and requirements are those
+ * of qmx_qmm_t_splitk without `out`; a NULL or short workspace is
+ * QMX_ERR_WORKSPACE. */
+int qmx_qmm_t_partials(const uint32_t* w_packed, const void* scales, const void* biases,
+                       const void* x, int M, int N, int K, int bits, int group_size,
+                       int dtype, int splits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* qmx_splitk_accumulate -- the second kernel of qmx_qmm_t_splitk on its own
+ * (the separate accumulate kernel of page "mlx PR 4682"):
+ * out[m][n] = round(sum over p = 0..splits-1, in that order, of
+ * workspace[p][m][n]), float32 sums rounded once to `dtype` (QMX_F16 or
+ * QMX_BF16).  workspace: splits*M*N float32, 16-byte aligned; out: M*N
+ * elements.  2 <= splits <= QMX_MAX_SPLITS. */
+int qmx_splitk_accumulate(const void* workspace, void* out, int M, int N, int splits, int dtype,
+                          void* stream);
+
 /* Bytes of float32 partials qmx_qmm_t_splitk needs: splits * M * N * 4
  * (0 for negative arguments). */
 size_t qmx_splitk_workspace_bytes(int M, int N, int splits);

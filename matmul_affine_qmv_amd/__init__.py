@@ -36,6 +36,9 @@ _EXPORTS = {
     "qmx_qmm_t": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_void_p]),
     "qmx_qmm_t_splitk": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7
                          + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_qmm_t_partials": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 7
+                           + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_splitk_accumulate": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + [ctypes.c_void_p]),
     "qmx_splitk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
     "qmx_matvec_q8_0": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
     "qmx_matvec_q4_k": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
@@ -115,7 +118,7 @@ def _need_cuda(*ts):
             raise ValueError("all tensors must be on the same device")
 
 
-def _affine_args(w_packed, scales, biases, x, bits, group_size, out):
+def _affine_args(w_packed, scales, biases, x, bits, group_size, out, need_out=True):
     if x.dim() != 2 or w_packed.dim() != 2:
         raise ValueError("x must be [M, K] and w_packed [N, K*bits/32]")
     if w_packed.dtype not in _WORD_DTYPES:
@@ -131,6 +134,9 @@ def _affine_args(w_packed, scales, biases, x, bits, group_size, out):
             raise ValueError(f"{name} must be [N, K/group_size] = {(N, G)}, got {tuple(t.shape)}")
         if t.dtype != x.dtype:
             raise ValueError(f"{name} must have x's dtype {x.dtype}")
+    if not need_out:
+        _need_cuda(w_packed, scales, biases, x)
+        return M, N, K, None
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != (M, N) or out.dtype != x.dtype:
@@ -175,6 +181,34 @@ def qmm_t_splitk(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64
                                   bits, group_size, _dtype_code(x), splits, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(x)),
            "qmx_qmm_t_splitk")
+    return out
+
+
+def qmm_t_partials(w_packed, scales, biases, x, *, bits=4, group_size=64, splits=2, workspace=None):
+    """float32 split-K partials [splits, M, N] via qmx_qmm_t_partials (the first
+    kernel of qmm_t_splitk alone)."""
+    M, N, K, _ = _affine_args(w_packed, scales, biases, x, bits, group_size, None, need_out=False)
+    need = splitk_workspace_bytes(M, N, splits)
+    workspace = _workspace(x, need, workspace)
+    _check(lib().qmx_qmm_t_partials(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), M, N, K, bits,
+                                    group_size, _dtype_code(x), splits, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(x)),
+           "qmx_qmm_t_partials")
+    return workspace.view(-1)[: splits * M * N].view(splits, M, N)
+
+
+def splitk_accumulate(workspace, out, splits):
+    """out[M, N] = the float32 partials summed over the split axis in order and
+    rounded once (qmx_splitk_accumulate)."""
+    if not (workspace.is_cuda and out.is_cuda):
+        raise ValueError("splitk_accumulate: tensors must be on the GPU")
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or not out.is_contiguous():
+        raise ValueError("splitk_accumulate: contiguous float32 workspace and contiguous out required")
+    M, N = out.shape
+    if workspace.numel() < splits * M * N:
+        raise ValueError("splitk_accumulate: workspace smaller than splits * M * N")
+    _check(lib().qmx_splitk_accumulate(_ptr(workspace), _ptr(out), M, N, splits, _dtype_code(out), _stream(out)),
+           "qmx_splitk_accumulate")
     return out
 
 

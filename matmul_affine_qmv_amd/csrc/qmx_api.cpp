@@ -162,6 +162,34 @@ size_t qmx_splitk_workspace_bytes(int M, int N, int splits) {
     return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
+int qmx_qmm_t_partials(const uint32_t* w_packed, const void* scales, const void* biases, const void* x,
+                       int M, int N, int K, int bits, int group_size, int dtype, int splits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (splits < 2 || splits > QMX_MAX_SPLITS) return QMX_ERR_SPLITS;
+    // the workspace stands in for `out` in the shared pointer checks
+    int rc = check_qmm(w_packed, scales, biases, x, workspace, M, N, K, bits, group_size, dtype, splits);
+    if (rc == QMX_ERR_NULL && !workspace && M > 0 && N > 0) return QMX_ERR_WORKSPACE;
+    if (rc) return rc;
+    if (splits > max_splits_for(K)) return QMX_ERR_SPLITS;
+    if (M == 0 || N == 0) return QMX_OK;
+    if (!workspace || !is_aligned(workspace, 16) || workspace_bytes < qmx_splitk_workspace_bytes(M, N, splits))
+        return QMX_ERR_WORKSPACE;
+    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, nullptr, static_cast<float*>(workspace), M,
+                                           N, K, bits, group_size, dtype, splits, static_cast<hipStream_t>(stream)));
+}
+
+int qmx_splitk_accumulate(const void* workspace, void* out, int M, int N, int splits, int dtype, void* stream) {
+    if (splits < 2 || splits > QMX_MAX_SPLITS) return QMX_ERR_SPLITS;
+    if (dtype != QMX_F16 && dtype != QMX_BF16) return QMX_ERR_DTYPE;
+    if (M < 0 || N < 0) return QMX_ERR_SHAPE;
+    if (M == 0 || N == 0) return QMX_OK;
+    if (!out) return QMX_ERR_NULL;
+    if (!workspace || !is_aligned(workspace, 16)) return QMX_ERR_WORKSPACE;
+    if (!is_aligned(out, 2)) return QMX_ERR_ALIGN;
+    return launch_status(qmx::launch_splitk_accum(static_cast<const float*>(workspace), out, splits,
+                                                  (size_t)M * N, dtype, static_cast<hipStream_t>(stream)));
+}
+
 int qmx_qmm_t_splitk(const uint32_t* w_packed, const void* scales, const void* biases, const void* x,
                      void* out, int M, int N, int K, int bits, int group_size, int dtype, int splits,
                      void* workspace, size_t workspace_bytes, void* stream) {

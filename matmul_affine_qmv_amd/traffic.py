@@ -1,0 +1,149 @@
+"""HBM traffic of one kernel from rocprofv3 counters, calibrated on a plain copy.
+
+The TCC counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are read in two
+separate counter runs (the hardware cannot collect both in one pass).  They
+are scaled by what the same counters read for a device-to-device copy of a
+known number of bytes, so that the result is in bytes of HBM traffic per
+launch.  Steps, each under rocprofv3 on the GPU:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D/cf -o run -- \\
+        python3 -m matmul_affine_qmv_amd.traffic copy --mib 256
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D/cw -o run -- \\
+        python3 -m matmul_affine_qmv_amd.traffic copy --mib 256
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D/kf -o run -- python3 bench.py --workload only:CALL ...
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D/kw -o run -- python3 bench.py --workload only:CALL ...
+
+then, on any machine:
+
+    python3 -m matmul_affine_qmv_amd.traffic summarize --dir D --call CALL --kernel SUBSTRING \\
+        --label LABEL --copy-mib 256 --out profiles/traffic_CALL.json
+
+The summary records a digest of the kernel sources; bench.py reports the
+traffic only while the sources still match it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (csrc/*), in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_values(run_dir: str, counter: str, kernel_substring: str):
+    """Per-dispatch values of `counter` for dispatches whose kernel name holds the substring."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    vals, names = [], set()
+    for path in files:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter or kernel_substring not in row["Kernel_Name"]:
+                    continue
+                vals.append(float(row["Counter_Value"]))
+                names.add(row["Kernel_Name"].split("(")[0].replace("void ", ""))
+    if not vals:
+        raise SystemExit(f"no {counter} values for '{kernel_substring}' under {run_dir}")
+    return vals, sorted(names)
+
+
+def run_copy(mib: int, reps: int) -> None:
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.full((n,), 1.5, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: reads n floats, writes n floats
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB {reps} times", flush=True)
+
+
+def summarize(args) -> dict:
+    copy_bytes = args.copy_mib * 2 ** 20
+    cf, _ = _counter_values(os.path.join(args.dir, "cf"), "FETCH_SIZE", args.copy_kernel)
+    cw, _ = _counter_values(os.path.join(args.dir, "cw"), "WRITE_SIZE", args.copy_kernel)
+    kf, names = _counter_values(os.path.join(args.dir, "kf"), "FETCH_SIZE", args.kernel)
+    kw, _ = _counter_values(os.path.join(args.dir, "kw"), "WRITE_SIZE", args.kernel)
+    # a copy of B bytes reads B and writes B: bytes per counted KiB
+    f_scale = copy_bytes / statistics.median(cf)
+    w_scale = copy_bytes / statistics.median(cw)
+    fetch = statistics.median(kf) * f_scale
+    write = statistics.median(kw) * w_scale
+    return {
+        "call": args.call,
+        "kernel_label": args.label,
+        "kernels": names,
+        "dispatches": {"fetch": len(kf), "write": len(kw)},
+        "fetch_size_kib_median": statistics.median(kf),
+        "write_size_kib_median": statistics.median(kw),
+        "copy_calibration": {"bytes": copy_bytes, "fetch_size_kib": statistics.median(cf),
+                             "write_size_kib": statistics.median(cw), "fetch_bytes_per_kib": f_scale,
+                             "write_bytes_per_kib": w_scale},
+        "fetch_bytes_per_launch": fetch,
+        "write_bytes_per_launch": write,
+        "traffic_bytes_per_launch": fetch + write,
+        "source_sha256": source_digest(),
+    }
+
+
+def kernel_stats_markdown(stats_csv: str, substring: str = "qmx::") -> str:
+    """rocprofv3 --stats kernel table (run_kernel_stats.csv) as markdown, library kernels only."""
+    out = ["| kernel | calls | avg µs | min µs | max µs |", "|---|---:|---:|---:|---:|"]
+    with open(stats_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            if substring not in row["Name"]:
+                continue
+            name = row["Name"].split("(")[0].replace("void ", "")
+            out.append(f"| `{name}` | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                       f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy", help="elementwise device-to-device copy of a known size (calibration)")
+    c.add_argument("--mib", type=int, default=256)
+    c.add_argument("--reps", type=int, default=10)
+    s = sub.add_parser("summarize", help="turn four counter runs into bytes per launch")
+    s.add_argument("--dir", required=True)
+    s.add_argument("--call", required=True)
+    s.add_argument("--kernel", required=True, help="substring of the kernel name to keep")
+    s.add_argument("--label", required=True, help="kernel label bench.py reports for this kernel")
+    s.add_argument("--copy-kernel", default="MulFunctor", help="substring of the copy kernel's name")
+    s.add_argument("--copy-mib", type=int, default=256)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("stats", help="markdown table of the library kernels in a --stats run")
+    t.add_argument("csv", help="run_kernel_stats.csv")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(kernel_stats_markdown(args.csv), end="")
+        return 0
+    if args.cmd == "copy":
+        run_copy(args.mib, args.reps)
+        return 0
+    res = summarize(args)
+    with open(args.out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -116,6 +116,32 @@ def test_splitk_validation():
 
 
 @fake_ptr_test
+def test_partials_and_accumulate_validation():
+    L = qmx.lib()
+
+    def parts(splits=4, ws=FAKE, wsb=1 << 30, M=16, N=64, K=4096, dt=BF16):
+        return L.qmx_qmm_t_partials(FAKE, FAKE, FAKE, FAKE, M, N, K, 4, 64, dt, splits, ws, wsb, None)
+
+    assert parts(splits=1) == ESPLITS
+    assert parts(splits=17) == ESPLITS
+    assert parts(splits=3, K=512) == ESPLITS
+    assert parts(ws=None) == EWS
+    assert parts(wsb=4 * 16 * 64 * 4 - 1) == EWS
+    assert parts(dt=F32) == EDTYPE
+    assert parts(M=0, ws=None) == OK
+    acc = L.qmx_splitk_accumulate
+    assert acc(FAKE, FAKE, 4, 4, 1, BF16, None) == ESPLITS
+    assert acc(FAKE, FAKE, 4, 4, 17, BF16, None) == ESPLITS
+    assert acc(FAKE, FAKE, 4, 4, 2, F32, None) == EDTYPE
+    assert acc(FAKE, FAKE, -1, 4, 2, BF16, None) == ESHAPE
+    assert acc(None, FAKE, 4, 4, 2, BF16, None) == EWS
+    assert acc(ctypes.c_void_p(0x10008), FAKE, 4, 4, 2, BF16, None) == EWS
+    assert acc(FAKE, None, 4, 4, 2, BF16, None) == ENULL
+    assert acc(FAKE, ctypes.c_void_p(0x10001), 4, 4, 2, BF16, None) == EALIGN
+    assert acc(None, None, 0, 4, 2, BF16, None) == OK
+
+
+@fake_ptr_test
 def test_block_validation():
     L = qmx.lib()
     assert L.qmx_matvec_q8_0(FAKE, FAKE, FAKE, 16, 48, None) == EGROUP

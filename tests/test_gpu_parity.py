@@ -175,6 +175,53 @@ def test_splitk_partials_match_partition_oracle(orc):
     assert np.array_equal(out64(y, dt), want)
 
 
+@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.BF16)])
+def test_partials_and_accumulate_entry_points(orc, bits, gs, dt):
+    """qmx_qmm_t_partials writes exactly the partition partials qmx_qmm_t_splitk
+    leaves in its workspace, and qmx_splitk_accumulate of those partials gives
+    qmx_qmm_t_splitk's output bit for bit."""
+    M, N, K, S = 33, 384, 2560, 4
+    say("partials + accumulate", M, N, K, bits, gs, dt, S)
+    c = qi.affine_case(M, N, K, bits, gs, dt, seed=1600 + bits + gs)
+    w, s, b, x = to_dev(c)
+    ws_a = torch.full((S * M * N,), float("nan"), dtype=torch.float32, device=DEV)
+    y = qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=S, workspace=ws_a)
+    parts = qmx.qmm_t_partials(w, s, b, x, bits=bits, group_size=gs, splits=S)
+    out = torch.empty_like(y)
+    qmx.splitk_accumulate(parts, out, S)
+    torch.cuda.synchronize()
+    assert torch.equal(parts.view(-1).view(torch.int32), ws_a.view(torch.int32))
+    assert torch.equal(out.view(torch.int16), y.view(torch.int16))
+    nkb = K // 128
+    host = parts.cpu().numpy().astype(np.float64)
+    for p in range(S):
+        kb0, kb1 = p * nkb // S, (p + 1) * nkb // S
+        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs,
+                                kb0 * 128 // gs, kb1 * 128 // gs)
+        assert_close(host[p], ref, qi.F32, orc, what=f"partial {p}")
+
+
+def test_accumulate_sums_in_order_and_rounds_once(orc):
+    """The accumulate kernel alone on float32 partials chosen so that the
+    summation order and a single rounding are visible: ascending float32 sums
+    of the partitions, then one round-to-nearest-even to the output type."""
+    M, N = 7, 130   # M*N not a multiple of 4: the element-wise tail path too
+    rng = np.random.Generator(np.random.PCG64(77))
+    for S in (2, 3, 16):
+        for dt in (qi.BF16, qi.F16):
+            say("accumulate", M, N, S, dt)
+            parts = (rng.standard_normal((S, M, N)) * rng.choice([1e-3, 1.0, 1e3], size=(S, M, N))).astype(np.float32)
+            ws = torch.from_numpy(parts.reshape(-1)).to(DEV)
+            out = torch.empty((M, N), dtype=TORCH_DT[dt], device=DEV)
+            qmx.splitk_accumulate(ws, out, S)
+            torch.cuda.synchronize()
+            acc = parts[0].copy()
+            for p in range(1, S):
+                acc = (acc + parts[p]).astype(np.float32)
+            want = orc.round(acc.astype(np.float64), dt)
+            assert np.array_equal(out64(out, dt), want)
+
+
 # ---------------------------------------------------------------- affine sweep (bits x gs x dtype x M)
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("gs", [32, 64, 128])
