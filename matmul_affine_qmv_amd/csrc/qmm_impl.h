@@ -25,8 +25,9 @@
 // * Codes are expanded in registers right before the MFMA into exact 16-bit
 //   integers in natural k order: fields are split into bytes, interleaved,
 //   and one v_perm per pair of codes sets a magic exponent byte above each
-//   (0x43qq is the bf16 value 128 + q, 0x64qq the f16 value 1024 + q).  The
-//   constant offset OFF*sum(x) this adds is removed in the group epilogue.
+//   (0x43qq is the bf16 value 128 + q, 0x64qq the f16 value 1024 + q).  f16
+//   pairs then drop the 1024 with one exact packed f16 subtraction; for bf16
+//   the constant offset 128*sum(x) is removed in the group epilogue.
 // * MFMA v_mfma_f32_16x16x32_{bf16,f16}: A = x fragment (16 rows of M),
 //   B = W codes (16 columns of N).  A group of GS codes is GS/32 k-steps
 //   accumulated into a fresh float32 tile; the same A fragments against an
@@ -64,8 +65,10 @@ struct QmmCfg {
     static constexpr int STAGE = X_BYTES + W_BYTES + SB_BYTES;
     static constexpr int NS = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
     static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
+    // Offset the expanded bf16 codes carry: 128 + q (q < 128); 8-bit bf16 codes are
+    // converted instead, and f16 codes have their 1024 removed exactly before the MFMA.
     static constexpr bool CVT8 = DT == DT_BF16 && BITS == 8;  // 128 + q is not exact in bf16
-    static constexpr float OFF = CVT8 ? 0.f : (DT == DT_F16 ? 1024.f : 128.f);
+    static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
     static constexpr int RED_BYTES = QMM_WAVES_N * MT * QMM_NB * 4 * 64 * 4;
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
@@ -100,13 +103,28 @@ __device__ constexpr uint32_t perm_sel(int i, int j) {
     return (uint32_t)i | (4u << 8) | ((uint32_t)j << 16) | (4u << 24);
 }
 
+// f16 pairs 1024 + q -> q, exactly (packed f16 subtraction).  Keeping the
+// offset would leave s * 1024 * sum(x) to cancel against the bias term in
+// float32, costing about ten bits of the group partial's precision.
+__device__ __forceinline__ uint32_t drop1024(uint32_t v) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 r = __builtin_bit_cast(h2, v) - h2{(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int DT>
+__device__ __forceinline__ u32x4 finish(u32x4 r) {
+    if constexpr (DT == DT_F16) return u32x4{drop1024(r.x), drop1024(r.y), drop1024(r.z), drop1024(r.w)};
+    else return r;
+}
+
 // Eight byte-held codes (bytes of e = c0 c1 c4 c5 and f = c2 c3 c6 c7) as
 // four pairs of 16-bit MFMA operands in natural order.
 template <int DT>
 __device__ __forceinline__ u32x4 magic_pairs(uint32_t e, uint32_t f) {
     constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
-    return u32x4{__builtin_amdgcn_perm(MB, e, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, f, perm_sel(0, 1)),
-                 __builtin_amdgcn_perm(MB, e, perm_sel(2, 3)), __builtin_amdgcn_perm(MB, f, perm_sel(2, 3))};
+    return finish<DT>(u32x4{__builtin_amdgcn_perm(MB, e, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, f, perm_sel(0, 1)),
+                            __builtin_amdgcn_perm(MB, e, perm_sel(2, 3)), __builtin_amdgcn_perm(MB, f, perm_sel(2, 3))});
 }
 
 // 8 consecutive 4-bit codes of one word (code i at bits 4i).
@@ -117,8 +135,8 @@ __device__ __forceinline__ u32x4 expand4(uint32_t w) {
     const uint32_t c0123 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
     const uint32_t c4567 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
     constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
-    return u32x4{__builtin_amdgcn_perm(MB, c0123, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c0123, perm_sel(2, 3)),
-                 __builtin_amdgcn_perm(MB, c4567, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c4567, perm_sel(2, 3))};
+    return finish<DT>(u32x4{__builtin_amdgcn_perm(MB, c0123, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c0123, perm_sel(2, 3)),
+                            __builtin_amdgcn_perm(MB, c4567, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c4567, perm_sel(2, 3))});
 }
 
 // 8 consecutive 2-bit codes held in the low 16 bits of h (code i at bits 2i).
@@ -134,8 +152,8 @@ template <int DT>
 __device__ __forceinline__ u32x4 expand8(uint32_t w0, uint32_t w1) {
     if constexpr (DT == DT_F16) {
         constexpr uint32_t MB = 0x64646464u;
-        return u32x4{__builtin_amdgcn_perm(MB, w0, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w0, perm_sel(2, 3)),
-                     __builtin_amdgcn_perm(MB, w1, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w1, perm_sel(2, 3))};
+        return finish<DT>(u32x4{__builtin_amdgcn_perm(MB, w0, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w0, perm_sel(2, 3)),
+                                __builtin_amdgcn_perm(MB, w1, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, w1, perm_sel(2, 3))});
     } else {
         // bf16 holds every integer up to 256 exactly: convert, keep the upper halves.
         auto pair = [](uint32_t a, uint32_t b) {
