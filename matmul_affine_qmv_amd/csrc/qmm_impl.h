@@ -44,7 +44,7 @@
 
 namespace qmx {
 
-template <int DT, int BITS, int GS, int MT>
+template <int DT, int BITS, int GS, int MT, bool SBV>
 struct QmmCfg {
     static constexpr int BM = 16 * MT;
     static constexpr int GPB = QMM_KB / GS;                   // groups per K block
@@ -58,23 +58,37 @@ struct QmmCfg {
     static constexpr int W_ROW = 16 * BITS;
     static constexpr int W_BYTES = QMM_BN * W_ROW;
     static constexpr int WPT = BITS == 4 ? 1 : 2;             // W copies per thread per block
-    // scales then biases, one 16-bit value per lane (zero-extended to 4 bytes in LDS)
+    // Scales then biases.  Staged per block, one 16-bit value per lane
+    // (zero-extended to 4 bytes in LDS), unless SBV: then the work-group's whole
+    // K range of both is copied once, before the ring, in 16-byte chunks.
     static constexpr int SB_VALUES = 2 * QMM_BN * GPB;
-    static constexpr int SBPT = (SB_VALUES + QMM_THREADS - 1) / QMM_THREADS;
+    static constexpr int SBPT = SBV ? 0 : (SB_VALUES + QMM_THREADS - 1) / QMM_THREADS;
     static constexpr int SB_BYTES = SBPT * QMM_THREADS * 4;
     static constexpr int STAGE = X_BYTES + W_BYTES + SB_BYTES;
-    static constexpr int NS = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
+    // ring depth: up to 4 stages, leaving SBV at least 12 KB for its chunks
+    static constexpr int RING_LDS = 160 * 1024 - (SBV ? 12 * 1024 : 0);
+    static constexpr int NS = RING_LDS / STAGE < 4 ? RING_LDS / STAGE : 4;
     static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
+    // SBV: 16-byte chunks (8 groups) per (scale/bias, column) held in LDS
+    static constexpr int SBV_CHUNKS = SBV ? ((160 * 1024 - NS * STAGE) / (2 * QMM_BN * 16) > 15
+                                                 ? 15 : (160 * 1024 - NS * STAGE) / (2 * QMM_BN * 16))
+                                          : 0;
+    static constexpr int SBV_BYTES = SBV_CHUNKS * 2 * QMM_BN * 16;
+    static constexpr bool CVT8 = DT == DT_BF16 && BITS == 8;  // 128 + q is not exact in bf16
     // Offset the expanded bf16 codes carry: 128 + q (q < 128); 8-bit bf16 codes are
     // converted instead, and f16 codes have their 1024 removed exactly before the MFMA.
-    static constexpr bool CVT8 = DT == DT_BF16 && BITS == 8;  // 128 + q is not exact in bf16
     static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
     static constexpr int RED_BYTES = QMM_WAVES_N * MT * QMM_NB * 4 * 64 * 4;
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
     static_assert(STAGE % 1024 == 0 && X_BYTES % 1024 == 0, "stage alignment");
+    static_assert(!SBV || SBV_CHUNKS >= 3, "room for the staged scales and biases");
 };
+
+// Largest chunk count the staged scale/bias copy of one work-group may need.
+template <int DT, int BITS, int GS, int MT>
+constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true>::SBV_CHUNKS; }
 
 // 8-value chunk of the 128-column block that lane group g feeds at k-step s.
 // Each step's 32 values lie inside one group of GS.  2-bit codes with GS >= 64
@@ -185,15 +199,15 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int DT, int BITS, int GS, int MT, bool SPLIT>
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
     const void* __restrict__ x, void* __restrict__ out, float* __restrict__ ws,
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
-    using C = QmmCfg<DT, BITS, GS, MT>;
+    using C = QmmCfg<DT, BITS, GS, MT, SBV>;
     constexpr int NB = QMM_NB;
     constexpr int NS = C::NS;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * C::STAGE + C::SBV_BYTES];
 
     // Hardware block h runs on XCD h % 8; give each XCD a contiguous range of tiles.
     const int h = blockIdx.x;
@@ -245,9 +259,22 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         }
         wsrc[j] = w + (size_t)min(n0 + R, N - 1) * row_words + q;
     }
+    // SBV: the K range's scales and biases as 16-byte chunks of 8 groups, chunk
+    // sb_c0 + c of every column at LDS slot (which*BN + col)*sb_nch + c.  An odd slot
+    // stride keeps the 16 columns a wave reads on distinct banks.
+    // When the range has an even chunk count, one more slot per column repeats its
+    // last chunk, so that the slot stride is odd.
+    int sb_c0 = 0, sb_nch = 0, sb_last = 0;
+    if constexpr (SBV) {
+        if (nk > 0) {
+            sb_c0 = (kb0 * C::GPB) / 8;
+            sb_last = (kb1 * C::GPB + 7) / 8 - 1 - sb_c0;
+            sb_nch = (sb_last + 1) | 1;
+        }
+    }
     // scales/biases: value v = 512j + tid (modulo the value count) is the scale (then
     // the bias) of column (v % (BN*GPB)) / GPB, group v % GPB, and lands at LDS word v.
-    const uint16_t* sbsrc[C::SBPT];
+    const uint16_t* sbsrc[C::SBPT > 0 ? C::SBPT : 1];
 #pragma unroll
     for (int j = 0; j < C::SBPT; ++j) {
         const int v = (QMM_THREADS * j + tid) % C::SB_VALUES;
@@ -284,10 +311,11 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     constexpr uint32_t ONE2 = DT == DT_F16 ? 0x3c003c00u : 0x3f803f80u;
     const u32x4 ones = u32x4{ONE2, ONE2, ONE2, ONE2};
 
-    auto compute = [&](int buf) {
+    auto compute = [&](int buf, int kb) {
         const unsigned char* X = smem + buf * C::STAGE;
         const unsigned char* Wl = X + C::X_BYTES;
         const uint32_t* SB = reinterpret_cast<const uint32_t*>(Wl + C::W_BYTES);
+        const uint16_t* SBVl = reinterpret_cast<const uint16_t*>(smem + NS * C::STAGE);
         // expand this wave's two k-steps of codes
         u32x4 bf[2][NB];
 #pragma unroll
@@ -328,8 +356,16 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
             for (int nf = 0; nf < NB; ++nf) {
                 const int col = wn * (NB * 16) + nf * 16 + lrow;
-                const uint32_t sr = SB[col * C::GPB + g];
-                const uint32_t br = SB[QMM_BN * C::GPB + col * C::GPB + g];
+                uint32_t sr, br;
+                if constexpr (SBV) {
+                    const int ga = kb * C::GPB + g;                   // group index within the row
+                    const int at = (col * sb_nch + (ga >> 3) - sb_c0) * 8 + (ga & 7);
+                    sr = SBVl[at];
+                    br = SBVl[QMM_BN * sb_nch * 8 + at];
+                } else {
+                    sr = SB[col * C::GPB + g];
+                    br = SB[QMM_BN * C::GPB + col * C::GPB + g];
+                }
                 const float s = DT == DT_F16 ? f16_bits_to_f32(sr) : bf16_bits_to_f32(sr);
                 const float b = DT == DT_F16 ? f16_bits_to_f32(br) : bf16_bits_to_f32(br);
                 sv[gp][nf] = s;
@@ -378,18 +414,41 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     // it waits for all), and the barrier publishes them.  The copies of block
     // i + NS - 1 then go into the stage that block i - 1 used, which every wave
     // finished reading before the barrier.
+    if constexpr (SBV) {
+        // one copy per (scale/bias, column, chunk), lane v at LDS slot v; issued before
+        // the ring so that the first stage's wait also covers them (copies of a wave
+        // complete in order)
+        const int lanes = 2 * QMM_BN * sb_nch;
+        unsigned char* base = smem + NS * C::STAGE;
+        for (int j = 0; j * QMM_THREADS < lanes; ++j) {
+            const int v = QMM_THREADS * j + tid;
+            if (v < lanes) {
+                const int which = v / (QMM_BN * sb_nch);
+                const int rem = v - which * (QMM_BN * sb_nch);
+                const int col = rem / sb_nch, ch = rem - col * sb_nch;
+                const uint16_t* src = static_cast<const uint16_t*>(which ? biases : scales) +
+                                      (size_t)min(n0 + col, N - 1) * G + 8 * (sb_c0 + min(ch, sb_last));
+                dma<16>(src, base + (QMM_THREADS * j + 64 * wave) * 16);
+            }
+        }
+    }
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
         if (p < nk) stage_load(kb0 + p, p);
-    int buf = 0;
-    for (int i = 0; i < nk; ++i) {
-        if (i + NS - 2 < nk)
-            stage_barrier<C::LPS * (NS - 2)>();
-        else
-            stage_barrier<0>();
-        if (i + NS - 1 < nk) stage_load(kb0 + i + NS - 1, buf == 0 ? NS - 1 : buf - 1);
-        compute(buf);
-        buf = buf == NS - 1 ? 0 : buf + 1;
+    // unrolled by NS so that every stage address is a constant
+    for (int base = 0; base < nk; base += NS) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int i = base + j;
+            if (i < nk) {
+                if (i + NS - 2 < nk)
+                    stage_barrier<C::LPS * (NS - 2)>();
+                else
+                    stage_barrier<0>();
+                if (i + NS - 1 < nk) stage_load(kb0 + i + NS - 1, (j + NS - 1) % NS);
+                compute(j, kb0 + i);
+            }
+        }
     }
     stage_barrier<0>();
 
@@ -424,6 +483,13 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             }
 }
 
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
+void qmm_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out, float* ws,
+            int M, int N, int K, int splits, int ntiles, int mtiles, int total, int per_xcd, hipStream_t st) {
+    hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV>), grid, dim3(QMM_THREADS), 0, st, w, s, b, x,
+                       out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd);
+}
+
 template <int DT, int BITS, int GS, int MT>
 hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int M, int N, int K, int splits, hipStream_t st) {
@@ -431,13 +497,22 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
     const int mtiles = qmm_mtiles_for(M);
     const int total = ntiles * mtiles * splits;
     const int per_xcd = (total + 7) / 8;
-    const dim3 grid(8 * per_xcd), block(QMM_THREADS);
-    if (splits > 1)
-        hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, true>), grid, block, 0, st, w, s, b, x, out, ws,
-                           M, N, K, splits, ntiles, mtiles, total, per_xcd);
-    else
-        hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, false>), grid, block, 0, st, w, s, b, x, out, ws,
-                           M, N, K, splits, ntiles, mtiles, total, per_xcd);
+    const dim3 grid(8 * per_xcd);
+    // Staged scales/biases need 16-byte aligned arrays, rows of whole 16-byte chunks
+    // (K/GS a multiple of 8) and a K range whose chunks (plus one for alignment and
+    // one for an odd count) fit the LDS left over.
+    const int G = K / GS, nkb = K / QMM_KB;
+    const int nk_max = (nkb + splits - 1) / splits;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0;
+    const bool sbv = aligned && K > 0 && G % 8 == 0 &&
+                     (nk_max * (QMM_KB / GS) + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT>();
+    if (splits > 1) {
+        if (sbv) qmm_go<DT, BITS, GS, MT, true, true>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+        else qmm_go<DT, BITS, GS, MT, true, false>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+    } else {
+        if (sbv) qmm_go<DT, BITS, GS, MT, false, true>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+        else qmm_go<DT, BITS, GS, MT, false, false>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+    }
     return hipGetLastError();
 }
 
