@@ -364,15 +364,28 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
 
 int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
 
-// Waves of one row tile that split its chunks: enough waves to give every CU
-// several, while each wave keeps at least 32 chunks.
+// Waves of one row tile that split its chunks.  Each wave walks its chunks in
+// rounds of 64 (one per lane), every round a dependent memory round trip.  Of
+// the splits whose waves all fit on the chip at once (about QMV_RESIDENT), the
+// one with the fewest chunk rounds per wave wins, the smaller on ties (less
+// cross-wave reduction); when none fits, the rows alone fill the chip.
+constexpr long QMV_RESIDENT = 6144;
+
 int qmv_ksplit_for(int M, int N, int K, int bits) {
     if (qmv_mt_for(M) != 1) return 1;
     const long waves = (long)((N + QMV_ROWS - 1) / QMV_ROWS);
-    const int chunks = K * bits / 128;
-    int ks = 1;
-    while (ks < 4 && waves * ks < 4096 && chunks / (2 * ks) >= 32) ks *= 2;
-    return ks;
+    const long chunks = (long)K * bits / 128;
+    int best = 1;
+    long best_rounds = -1;
+    for (int ks = 1; ks <= 4; ks *= 2) {
+        if (waves * ks > QMV_RESIDENT || (ks > 1 && chunks / ks < 16)) break;
+        const long rounds = (chunks + 64 * ks - 1) / (64 * ks);
+        if (best_rounds < 0 || rounds < best_rounds) {
+            best_rounds = rounds;
+            best = ks;
+        }
+    }
+    return best;
 }
 
 template <int DT, int BITS, int GS, int MT, int KS>
