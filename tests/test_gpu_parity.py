@@ -222,6 +222,37 @@ def test_accumulate_sums_in_order_and_rounds_once(orc):
             assert np.array_equal(out64(out, dt), want)
 
 
+@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.F16)])
+def test_scale_bias_alignment_paths(orc, bits, gs, dt):
+    """Scales/biases that start 2 bytes past a 16-byte boundary cannot be staged in
+    16-byte chunks; the per-block path must give the same bits as the staged one."""
+    M, N, K, S = 40, 256, 4096, 4
+    say("scale/bias alignment", M, N, K, bits, gs, dt, S)
+    c = qi.affine_case(M, N, K, bits, gs, dt, seed=1700 + bits + gs)
+    w, s, b, x = to_dev(c)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    s2, b2 = shifted(s), shifted(b)
+    assert s2.data_ptr() % 16 != 0
+    for route, kw in (("qmm_t", {}), ("splitk", {"splits": S})):
+        y_a = run(route, w, s, b, x, bits, gs, **kw)
+        y_b = run(route, w, s2, b2, x, bits, gs, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(y_a.view(torch.int16), y_b.view(torch.int16)), route
+        assert_close(out64(y_b, dt), orc.affine_case(c), dt, orc, what=f"{route} shifted scales")
+
+
+def test_splitk_many_m_tiles(orc):
+    """Split-K with three 128-row tiles of x (M = 300) and a ragged last tile."""
+    check_affine(orc, "splitk", 300, 384, 2048, 4, 64, qi.BF16, seed=1800, splits=4, reruns=1)
+    check_affine(orc, "splitk", 300, 200, 2560, 4, 32, qi.F16, seed=1801, splits=5)
+
+
 # ---------------------------------------------------------------- affine sweep (bits x gs x dtype x M)
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("gs", [32, 64, 128])
