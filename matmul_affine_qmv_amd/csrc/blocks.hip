@@ -3,58 +3,75 @@
 // Formats and arithmetic follow page "hanzo-kernel src/quant.rs" (Q8_0
 // packed layout: 9 words per 32 weights; Q4_K: 144-byte super-blocks with
 // 6-bit sub-block scales and mins).  Both kernels are weight-bandwidth
-// bound; each wave owns 4 output rows so every x value it loads is used
-// four times, accumulates in float32 and ends with a fixed-order wave
-// reduction.
+// bound.  A work-group of 4 waves owns 16 output rows, 4 per wave, and walks
+// K in rounds of 2048 values: the round's float32 x is loaded once per
+// work-group (two 16-byte loads per thread) and shared through LDS, so x
+// costs a quarter of a weight row's worth of loads instead of as much as the
+// weights themselves.  Accumulation is float32 and each row ends with a
+// fixed-order wave reduction.
 #include "qmx_device.h"
 #include "qmx_internal.h"
 
 namespace qmx {
 
-constexpr int BLK_ROWS = 4;
+constexpr int BLK_ROWS = 4;                         // output rows per wave
+constexpr int BLK_WAVES = 4;                        // waves per work-group
+constexpr int BLK_THREADS = 64 * BLK_WAVES;
+constexpr int BLK_ROUND = 2048;                     // x values per round (8 KB)
 
-// ---------------------------------------------------------------- Q8_0
-// Lane l takes blocks l, l+64, ... of its rows.  A signed byte q is read as
-// the unsigned byte q ^ 0x80 = q + 128, and the 128 * sum(x) it adds is taken
-// off once per block: sum_i q_i x_i = sum_i (q_i + 128) x_i - 128 sum_i x_i.
-__global__ __launch_bounds__(64) void q8_0_kernel(const uint32_t* __restrict__ wb,
-                                                  const float* __restrict__ x,
-                                                  float* __restrict__ out, int N, int K) {
-    const int lane = threadIdx.x;
-    const int n0 = blockIdx.x * BLK_ROWS;
-    const int nb = K / 32;
-    float acc[BLK_ROWS] = {0.f, 0.f, 0.f, 0.f};
+// The round's x as 512 16-byte pieces.  Piece u (x values 4u..4u+3 of the
+// round) is stored at slot u ^ ((u >> 4) & 15), which spreads the pieces the
+// lanes of a wave read together over distinct banks.
+__device__ __forceinline__ int x_slot(int u) { return u ^ ((u >> 4) & 15); }
 
-    for (int b = lane; b < nb; b += 64) {
-        float xv[32];
-        const u32x4* xp = reinterpret_cast<const u32x4*>(x + 32 * (size_t)b);
+// Load the round starting at x value k0 (clamped into [0, K)): thread t takes
+// pieces 2t and 2t+1.
+__device__ __forceinline__ void x_round_load(const float* __restrict__ x, int K, int k0, int tid, u32x4 (&v)[2]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const u32x4 d = xp[i];
-            xv[4 * i + 0] = __uint_as_float(d.x);
-            xv[4 * i + 1] = __uint_as_float(d.y);
-            xv[4 * i + 2] = __uint_as_float(d.z);
-            xv[4 * i + 3] = __uint_as_float(d.w);
-        }
-        float xs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) xs += xv[i];
-#pragma unroll
-        for (int r = 0; r < BLK_ROWS; ++r) {
-            const int n = min(n0 + r, N - 1);
-            const uint32_t* blk = wb + ((size_t)n * nb + b) * 9;
-            const float d = f16_bits_to_f32(blk[0] & 0xffffu);
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t wd = blk[1 + j] ^ 0x80808080u;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s = fmaf((float)((wd >> (8 * i)) & 0xffu), xv[4 * j + i], s);
-            }
-            acc[r] = fmaf(d, fmaf(-128.f, xs, s), acc[r]);
-        }
+    for (int j = 0; j < 2; ++j) {
+        const int e = min(k0 + 4 * (2 * tid + j), K - 4);
+        v[j] = *reinterpret_cast<const u32x4*>(x + e);
     }
+}
 
+__device__ __forceinline__ void x_round_store(u32x4* buf, int tid, const u32x4 (&v)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) buf[x_slot(2 * tid + j)] = v[j];
+}
+
+__device__ __forceinline__ void x_piece(const u32x4* buf, int u, float* dst) {
+    const u32x4 d = buf[x_slot(u)];
+    dst[0] = __uint_as_float(d.x);
+    dst[1] = __uint_as_float(d.y);
+    dst[2] = __uint_as_float(d.z);
+    dst[3] = __uint_as_float(d.w);
+}
+
+// Per-round skeleton shared by both formats: while round r is consumed, the
+// weights of round r + 1 are already requested into registers and its x is
+// loaded, then staged into the other LDS buffer; one barrier per round.
+template <typename WStage, typename Load, typename Consume>
+__device__ __forceinline__ void blk_rounds(const float* __restrict__ x, int K, int rounds, int tid,
+                                           u32x4 (*xl)[BLK_ROUND / 4], Load&& load, Consume&& consume) {
+    u32x4 v[2];
+    WStage cur, nxt;
+    load(0, cur);
+    x_round_load(x, K, 0, tid, v);
+    x_round_store(xl[0], tid, v);
+    __syncthreads();
+    for (int rd = 0; rd < rounds; ++rd) {
+        // past the last round the loads repeat the last round and are never used
+        const int rn = min(rd + 1, rounds - 1);
+        load(rn, nxt);
+        x_round_load(x, K, rn * BLK_ROUND, tid, v);
+        consume(xl[rd & 1], rd, cur);
+        x_round_store(xl[(rd + 1) & 1], tid, v);
+        __syncthreads();
+        cur = nxt;
+    }
+}
+
+__device__ __forceinline__ void blk_store(float (&acc)[BLK_ROWS], int lane, int n0, int N, float* __restrict__ out) {
     float mine = 0.f;
 #pragma unroll
     for (int r = 0; r < BLK_ROWS; ++r) {
@@ -64,12 +81,63 @@ __global__ __launch_bounds__(64) void q8_0_kernel(const uint32_t* __restrict__ w
     if (lane < BLK_ROWS && n0 + lane < N) out[n0 + lane] = mine;
 }
 
+// ---------------------------------------------------------------- Q8_0
+// In round rd, lane l takes block 64*rd + l of its rows (x values 32l..32l+31
+// of the round).  A signed byte q is read as the unsigned byte q ^ 0x80 =
+// q + 128, and the 128 * sum(x) it adds is taken off once per block:
+// sum_i q_i x_i = sum_i (q_i + 128) x_i - 128 sum_i x_i.
+__global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __restrict__ wb,
+                                                           const float* __restrict__ x,
+                                                           float* __restrict__ out, int N, int K) {
+    __shared__ u32x4 xl[2][BLK_ROUND / 4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
+    const int nb = K / 32;
+    float acc[BLK_ROWS] = {0.f, 0.f, 0.f, 0.f};
+
+    struct WS { uint32_t w[BLK_ROWS][9]; };
+    if (nb > 0) {
+        auto load = [&](int rd, WS& st) {
+            const int b = min(64 * rd + lane, nb - 1);
+#pragma unroll
+            for (int r = 0; r < BLK_ROWS; ++r) {
+                const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 9;
+#pragma unroll
+                for (int j = 0; j < 9; ++j) st.w[r][j] = blk[j];
+            }
+        };
+        blk_rounds<WS>(x, K, (nb + 63) / 64, tid, xl, load, [&](const u32x4* buf, int rd, const WS& st) {
+            const bool act = 64 * rd + lane < nb;
+            float xv[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x_piece(buf, 8 * lane + i, xv + 4 * i);
+            float xs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) xs += xv[i];
+#pragma unroll
+            for (int r = 0; r < BLK_ROWS; ++r) {
+                const float d = f16_bits_to_f32(st.w[r][0] & 0xffffu);
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t wd = st.w[r][1 + j] ^ 0x80808080u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s = fmaf((float)((wd >> (8 * i)) & 0xffu), xv[4 * j + i], s);
+                }
+                const float add = d * fmaf(-128.f, xs, s);
+                acc[r] += act ? add : 0.f;
+            }
+        });
+    }
+    blk_store(acc, lane, n0, N, out);
+}
+
 // ---------------------------------------------------------------- Q4_K
-// Eight lanes share a super-block: lane part j (0..7) reads quant bytes
-// [16j, 16j+16), i.e. g = j/2 and i in [16(j%2), 16(j%2)+16): low nibbles
-// are elements 64g+i of sub-block 2g, high nibbles elements 64g+32+i of
-// sub-block 2g+1.  Per sub-block part the sum of q*x and the sum of x are
-// formed once; the weight d*sc*q - dmin*m is applied as
+// In round rd, eight lanes share super-block 8*rd + l/8: lane part j (0..7)
+// reads quant bytes [16j, 16j+16), i.e. g = j/2 and i in [16(j%2), 16(j%2)+16):
+// low nibbles are elements 64g+i of sub-block 2g, high nibbles elements
+// 64g+32+i of sub-block 2g+1.  Per sub-block part the sum of q*x and the sum
+// of x are formed once; the weight d*sc*q - dmin*m is applied as
 // d*sc*sum(q x) - dmin*m*sum(x).
 __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
                                               uint32_t& sc, uint32_t& mn) {
@@ -83,78 +151,77 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
     mn = j < 4 ? lo_mn : hi_mn;
 }
 
-__global__ __launch_bounds__(64) void q4_k_kernel(const uint32_t* __restrict__ wb,
-                                                  const float* __restrict__ x,
-                                                  float* __restrict__ out, int N, int K) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __restrict__ wb,
+                                                           const float* __restrict__ x,
+                                                           float* __restrict__ out, int N, int K) {
+    __shared__ u32x4 xl[2][BLK_ROUND / 4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = lane >> 3, part = lane & 7;
     const int g = part >> 1, t0 = (part & 1) * 16;
-    const int n0 = blockIdx.x * BLK_ROWS;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
     const int nb = K / 256;
     float acc[BLK_ROWS] = {0.f, 0.f, 0.f, 0.f};
 
-    for (int b = slot; b < nb; b += 8) {
-        float xl[16], xh[16];
-        const float* xb = x + 256 * (size_t)b + 64 * g + t0;
+    struct WS { u32x4 hdr[BLK_ROWS], qw[BLK_ROWS]; };
+    if (nb > 0) {
+        auto load = [&](int rd, WS& st) {
+            const int b = min(8 * rd + slot, nb - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 dl = reinterpret_cast<const u32x4*>(xb)[i];
-            const u32x4 dh = reinterpret_cast<const u32x4*>(xb + 32)[i];
-            xl[4 * i + 0] = __uint_as_float(dl.x); xl[4 * i + 1] = __uint_as_float(dl.y);
-            xl[4 * i + 2] = __uint_as_float(dl.z); xl[4 * i + 3] = __uint_as_float(dl.w);
-            xh[4 * i + 0] = __uint_as_float(dh.x); xh[4 * i + 1] = __uint_as_float(dh.y);
-            xh[4 * i + 2] = __uint_as_float(dh.z); xh[4 * i + 3] = __uint_as_float(dh.w);
-        }
-        float xsl = 0.f, xsh = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { xsl += xl[i]; xsh += xh[i]; }
-
-#pragma unroll
-        for (int r = 0; r < BLK_ROWS; ++r) {
-            const int n = min(n0 + r, N - 1);
-            const uint32_t* blk = wb + ((size_t)n * nb + b) * 36;
-            const u32x4 hdr = *reinterpret_cast<const u32x4*>(blk);
-            const u32x4 qw = *reinterpret_cast<const u32x4*>(blk + 4 + 4 * part);
-            const float d = f16_bits_to_f32(hdr.x & 0xffffu);
-            const float dmin = f16_bits_to_f32(hdr.x >> 16);
-            uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * g, sc_lo, mn_lo);
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * g + 1, sc_hi, mn_hi);
-            float sl = 0.f, sh = 0.f;
-            const uint32_t qws[4] = {qw.x, qw.y, qw.z, qw.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sl = fmaf((float)((lo >> (8 * i)) & 0xffu), xl[4 * k + i], sl);
-                    sh = fmaf((float)((hi >> (8 * i)) & 0xffu), xh[4 * k + i], sh);
-                }
+            for (int r = 0; r < BLK_ROWS; ++r) {
+                const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 36;
+                st.hdr[r] = *reinterpret_cast<const u32x4*>(blk);
+                st.qw[r] = *reinterpret_cast<const u32x4*>(blk + 4 + 4 * part);
             }
-            const float qpart = fmaf((float)sc_lo, sl, (float)sc_hi * sh);
-            const float mpart = fmaf((float)mn_lo, xsl, (float)mn_hi * xsh);
-            acc[r] = fmaf(d, qpart, fmaf(-dmin, mpart, acc[r]));
-        }
-    }
-
-    float mine = 0.f;
+        };
+        blk_rounds<WS>(x, K, (nb + 7) / 8, tid, xl, load, [&](const u32x4* buf, int rd, const WS& st) {
+            const bool act = 8 * rd + slot < nb;
+            float xlo[16], xhi[16];
+            const int u0 = (256 * slot + 64 * g + t0) / 4;   // first piece of the low half
 #pragma unroll
-    for (int r = 0; r < BLK_ROWS; ++r) {
-        const float t = wave_sum(acc[r]);
-        if (lane == r) mine = t;
+            for (int i = 0; i < 4; ++i) {
+                x_piece(buf, u0 + i, xlo + 4 * i);
+                x_piece(buf, u0 + 8 + i, xhi + 4 * i);
+            }
+            float xsl = 0.f, xsh = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { xsl += xlo[i]; xsh += xhi[i]; }
+#pragma unroll
+            for (int r = 0; r < BLK_ROWS; ++r) {
+                const float d = f16_bits_to_f32(st.hdr[r].x & 0xffffu);
+                const float dmin = f16_bits_to_f32(st.hdr[r].x >> 16);
+                uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
+                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, 2 * g, sc_lo, mn_lo);
+                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, 2 * g + 1, sc_hi, mn_hi);
+                float sl = 0.f, sh = 0.f;
+                const uint32_t qws[4] = {st.qw[r].x, st.qw[r].y, st.qw[r].z, st.qw[r].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sl = fmaf((float)((lo >> (8 * i)) & 0xffu), xlo[4 * k + i], sl);
+                        sh = fmaf((float)((hi >> (8 * i)) & 0xffu), xhi[4 * k + i], sh);
+                    }
+                }
+                const float qpart = fmaf((float)sc_lo, sl, (float)sc_hi * sh);
+                const float mpart = fmaf((float)mn_lo, xsl, (float)mn_hi * xsh);
+                const float add = fmaf(d, qpart, -dmin * mpart);
+                acc[r] += act ? add : 0.f;
+            }
+        });
     }
-    if (lane < BLK_ROWS && n0 + lane < N) out[n0 + lane] = mine;
+    blk_store(acc, lane, n0, N, out);
 }
 
 hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
-    const dim3 grid((N + BLK_ROWS - 1) / BLK_ROWS);
-    hipLaunchKernelGGL(q8_0_kernel, grid, dim3(64), 0, st, w, x, out, N, K);
+    const dim3 grid((N + BLK_WAVES * BLK_ROWS - 1) / (BLK_WAVES * BLK_ROWS));
+    hipLaunchKernelGGL(q8_0_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
 }
 
 hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
-    const dim3 grid((N + BLK_ROWS - 1) / BLK_ROWS);
-    hipLaunchKernelGGL(q4_k_kernel, grid, dim3(64), 0, st, w, x, out, N, K);
+    const dim3 grid((N + BLK_WAVES * BLK_ROWS - 1) / (BLK_WAVES * BLK_ROWS));
+    hipLaunchKernelGGL(q4_k_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
 }
 
