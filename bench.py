@@ -321,7 +321,7 @@ def cpu_baseline(calls, sets, target_s):
         "kind": "oracle",
         "sample": (f"float64 C oracle (OpenMP) on an evenly spaced sample of output columns of every call "
                    f"(about {100 * frac:.1f}% of columns after the first call), input set 0; "
-                   f"bytes scaled by the sampled fraction; {done_s:.1f} s of CPU time"),
+                   f"bytes scaled by the sampled fraction; {done_s:.1f} s wall time on {orc.num_threads()} threads"),
         "parity_ok": bool(worst[2]) if worst else None,
         "parity_worst": {"call": worst[0], "rel_l2_over_gate": worst[1]} if worst else None,
     }
@@ -332,7 +332,7 @@ def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on exactly one GPU "
-              f"(the hot path would shard across GPUs by output rows; see the design notes)", file=sys.stderr)
+              f"(the hot path would shard across GPUs by output rows of W)", file=sys.stderr)
         return 2
     import torch
 
