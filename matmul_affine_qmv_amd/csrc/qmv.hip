@@ -23,6 +23,8 @@
 //   bf16 x) use per-code conversion and float32 FMA.
 // * The final reductions are fixed xor-butterflies, so results do not change
 //   from run to run.
+#include <algorithm>
+
 #include "qmx_device.h"
 #include "qmx_internal.h"
 
@@ -143,10 +145,54 @@ struct QmvStage {
     u32x4 x[MT][XQ];
 };
 
+// Buffer resource over [p, p + bytes) (bytes clamped to 32 bits); every offset
+// used below stays inside the array, so the range check never trims a load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                             (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes),
+                                             0x00020000);
+}
+
 template <int DT>
-__device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
-    if constexpr (DT == DT_F32) return static_cast<const uint32_t*>(p)[i];
-    else return static_cast<const uint16_t*>(p)[i];
+__device__ __forceinline__ uint32_t buffer_raw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (DT == DT_F32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Where a lane's loads come from.  Every array is addressed through a buffer
+// resource based at the work-group's first row; a lane's byte offsets for its
+// first chunk are fixed (voffset) and each round adds the same scalar offset to
+// all lanes (soffset), so no per-round address arithmetic runs on the vector ALU.
+template <int DT, int BITS, int GS, int MT>
+struct QmvAddr {
+    static constexpr int R = QMV_ROWS;
+    static constexpr int EB = DT == DT_F32 ? 4 : 2;
+    __amdgpu_buffer_rsrc_t w, s, b, x;
+    int vw[R], vsb[R], vx[MT];
+};
+
+template <int DT, int BITS, int GS, int MT>
+__device__ __forceinline__ void qmv_load(QmvStage<DT, BITS, GS, MT>& st, const QmvAddr<DT, BITS, GS, MT>& ad,
+                                         int sw, int ssb, int sx) {
+    using S = QmvStage<DT, BITS, GS, MT>;
+    constexpr int EB = QmvAddr<DT, BITS, GS, MT>::EB;
+    // issued in the order the arithmetic first needs them (x, then the rows, then
+    // the group epilogue's scales and biases), so its waits can be partial
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < S::XQ; ++i)
+            st.x[m][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.x, ad.vx[m] + 16 * i, sx, 0));
+#pragma unroll
+    for (int r = 0; r < S::R; ++r)
+        st.w[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.w, ad.vw[r], sw, 0));
+#pragma unroll
+    for (int r = 0; r < S::R; ++r)
+#pragma unroll
+        for (int p = 0; p < S::PARTS; ++p) {
+            st.s[r][p] = buffer_raw<DT>(ad.s, ad.vsb[r] + p * EB, ssb);
+            st.b[r][p] = buffer_raw<DT>(ad.b, ad.vsb[r] + p * EB, ssb);
+        }
 }
 
 template <int DT>
@@ -154,35 +200,6 @@ __device__ __forceinline__ float raw_to_f32(uint32_t v) {
     if constexpr (DT == DT_F32) return __uint_as_float(v);
     else if constexpr (DT == DT_F16) return f16_bits_to_f32(v);
     else return bf16_bits_to_f32(v);
-}
-
-template <int DT, int BITS, int GS, int MT>
-__device__ __forceinline__ void qmv_load(QmvStage<DT, BITS, GS, MT>& st, const uint32_t* __restrict__ w,
-                                         const void* __restrict__ scales, const void* __restrict__ biases,
-                                         const void* __restrict__ x, int c, int n0, int N, int m0, int mcount,
-                                         int K, int G, size_t row_words) {
-    using S = QmvStage<DT, BITS, GS, MT>;
-    const int g0 = (c * S::CPC) / GS;
-#pragma unroll
-    for (int r = 0; r < S::R; ++r) {
-        const int n = min(n0 + r, N - 1);   // rows past N are computed but never stored
-        st.w[r] = *reinterpret_cast<const u32x4*>(w + (size_t)n * row_words + 4 * (size_t)c);
-#pragma unroll
-        for (int p = 0; p < S::PARTS; ++p) {
-            const size_t gi = (size_t)n * G + g0 + p;
-            st.s[r][p] = load_raw<DT>(scales, gi);
-            st.b[r][p] = load_raw<DT>(biases, gi);
-        }
-    }
-    constexpr int EB = DT == DT_F32 ? 4 : 2;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const int mm = m < mcount ? m : 0;   // rows past M reuse row m0; never stored
-        const unsigned char* xp = static_cast<const unsigned char*>(x) +
-                                  ((size_t)(m0 + mm) * K + (size_t)c * S::CPC) * EB;
-#pragma unroll
-        for (int i = 0; i < S::XQ; ++i) st.x[m][i] = reinterpret_cast<const u32x4*>(xp)[i];
-    }
 }
 
 // Word j (0..3) of a 16-byte chunk.
@@ -303,22 +320,46 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
         }
 }
 
-template <int DT, int BITS, int GS, int MT, int KSPLIT>
+template <int DT, int BITS, int GS, int MT, int KSPLIT, int RG>
 __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __restrict__ w,
                                                           const void* __restrict__ scales,
                                                           const void* __restrict__ biases,
                                                           const void* __restrict__ x,
                                                           void* __restrict__ out, int M, int N, int K) {
     constexpr int R = QMV_ROWS;
+    constexpr int LP = 64 / RG;   // lanes per row group
     using S = QmvStage<DT, BITS, GS, MT>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * R;
+    const int lp = lane / LP, ll = lane % LP;
+    const int nw = blockIdx.x * RG * R;          // first row of the work-group
+    const int n0 = nw + lp * R;                   // first row of this lane's row group
     const int m0 = blockIdx.y * MT;
     const int mcount = min(MT, M - m0);
     const int G = K / GS;
     const int chunks = K / S::CPC;
-    const size_t row_words = (size_t)K * BITS / 32;
+    const size_t row_bytes = (size_t)K * BITS / 8;
     const int c1 = (int)((long)(wave + 1) * chunks / KSPLIT);
+    int c = (int)((long)wave * chunks / KSPLIT) + ll;
+
+    // rows past N repeat row N - 1 and x rows past M repeat row m0; neither is stored
+    using A = QmvAddr<DT, BITS, GS, MT>;
+    constexpr int EB = A::EB;
+    A ad;
+    ad.w = buffer_over(reinterpret_cast<const unsigned char*>(w) + (size_t)nw * row_bytes, (size_t)(N - nw) * row_bytes);
+    ad.s = buffer_over(static_cast<const unsigned char*>(scales) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
+    ad.b = buffer_over(static_cast<const unsigned char*>(biases) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
+    ad.x = buffer_over(static_cast<const unsigned char*>(x) + (size_t)m0 * K * EB, (size_t)(M - m0) * K * EB);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int rr = min(n0 + r, N - 1) - nw;
+        ad.vw[r] = (int)((size_t)rr * row_bytes) + 16 * c;
+        ad.vsb[r] = (rr * G + (c * S::CPC) / GS) * EB;
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * K + c * S::CPC) * EB;
+    // per-round scalar steps
+    constexpr int STEP_W = LP * 16, STEP_SB = LP * S::CPC / GS * EB, STEP_X = LP * S::CPC * EB;
+    static_assert((LP * S::CPC) % GS == 0, "a round advances by whole groups");
 
     float acc[R][MT];
 #pragma unroll
@@ -326,89 +367,110 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
-    int c = (int)((long)wave * chunks / KSPLIT) + lane;
     // One chunk in flight per wave: the register budget goes to occupancy
     // (6-7 waves per SIMD), which overlaps loads and arithmetic better on
     // this kernel than a second register set at half the occupancy.
-    for (; c < c1; c += 64) {
+    for (int round = 0; c < c1; c += LP, ++round) {
         S a;
-        qmv_load(a, w, scales, biases, x, c, n0, N, m0, mcount, K, G, row_words);
+        qmv_load(a, ad, round * STEP_W, round * STEP_SB, round * STEP_X);
         qmv_consume(a, acc);
     }
 
+    // sums over the LP lanes of each row group (fixed xor butterflies)
     float mine = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const float tot = wave_sum(acc[r][m]);
-            if (lane == r * MT + m) mine = tot;
+            float tot = acc[r][m];
+#pragma unroll
+            for (int off = LP / 2; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+            if (ll == r * MT + m) mine = tot;
         }
     if constexpr (KSPLIT > 1) {
-        __shared__ float part[KSPLIT][R * MT];
-        if (lane < R * MT) part[wave][lane] = mine;
+        __shared__ float part[KSPLIT][RG * R * MT];
+        if (ll < R * MT) part[wave][lp * R * MT + ll] = mine;
         __syncthreads();
         if (wave != 0) return;
-        if (lane < R * MT) {
-            float t = part[0][lane];
+        if (ll < R * MT) {
+            float t = part[0][lp * R * MT + ll];
 #pragma unroll
-            for (int k = 1; k < KSPLIT; ++k) t += part[k][lane];
+            for (int k = 1; k < KSPLIT; ++k) t += part[k][lp * R * MT + ll];
             mine = t;
         }
     }
-    if (lane < R * MT) {
-        const int r = lane / MT, m = lane % MT;
+    if (ll < R * MT) {
+        const int r = ll / MT, m = ll % MT;
         if (n0 + r < N && m < mcount) store_elem<DT>(out, (size_t)(m0 + m) * N + n0 + r, mine);
     }
 }
 
 int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
 
-// Waves of one row tile that split its chunks.  Each wave walks its chunks in
-// rounds of 64 (one per lane), every round a dependent memory round trip.  Of
-// the splits whose waves all fit on the chip at once (about QMV_RESIDENT), the
-// one with the fewest chunk rounds per wave wins, the smaller on ties (less
-// cross-wave reduction); when none fits, the rows alone fill the chip.
-constexpr long QMV_RESIDENT = 6144;
+// Work split of an M = 1 matvec: KS waves of one work-group split the chunks of
+// the same rows, and RG row groups of QMV_ROWS rows share one wave (64 / RG
+// lanes each).  Each wave walks its chunks in rounds of 64 / RG (one per lane),
+// every round a dependent memory round trip.
+struct QmvSplit {
+    int ks, rg;
+};
 
-int qmv_ksplit_for(int M, int N, int K, int bits) {
-    if (qmv_mt_for(M) != 1) return 1;
-    const long waves = (long)((N + QMV_ROWS - 1) / QMV_ROWS);
+// Measured on the chip: a wave-round (one round of one wave, whatever its lane
+// use) costs about 1 us of a SIMD's time when the loads stream, and a wave's
+// rounds run one after another at about 1.6 us each when few waves are in
+// flight; each extra wave of a work-group adds its share of the cross-wave sum.
+// The split with the lowest max(wave-rounds per SIMD * 1 us, rounds * 1.6 us)
+// + 0.15 us * KS wins, the one with fewer rounds on ties.
+QmvSplit qmv_split_for(int M, int N, int K, int bits) {
+    if (qmv_mt_for(M) != 1) return {1, 1};
+    static constexpr QmvSplit kCands[] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {4, 1}, {5, 2}, {5, 4}};
     const long chunks = (long)K * bits / 128;
-    int best = 1;
-    long best_rounds = -1;
-    for (int ks = 1; ks <= 4; ks *= 2) {
-        if (waves * ks > QMV_RESIDENT || (ks > 1 && chunks / ks < 16)) break;
-        const long rounds = (chunks + 64 * ks - 1) / (64 * ks);
-        if (best_rounds < 0 || rounds < best_rounds) {
+    QmvSplit best = {1, 1};
+    double best_t = -1.0;
+    long best_rounds = 0;
+    for (const QmvSplit& c : kCands) {
+        const long per_wave = (chunks + c.ks - 1) / c.ks;
+        if (c.ks > 1 && per_wave < 16) continue;
+        const long lanes = 64 / c.rg;
+        const long rounds = (per_wave + lanes - 1) / lanes;
+        const long waves = (long)((N + QMV_ROWS * c.rg - 1) / (QMV_ROWS * c.rg)) * c.ks;
+        const double t = std::max((double)(waves * rounds) / 1024.0, 1.6 * (double)rounds) + 0.15 * c.ks;
+        if (best_t < 0 || t < best_t - 1e-9 || (t < best_t + 1e-9 && rounds < best_rounds)) {
+            best = c;
+            best_t = t;
             best_rounds = rounds;
-            best = ks;
         }
     }
     return best;
 }
 
-template <int DT, int BITS, int GS, int MT, int KS>
-static void qmv_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                   int M, int N, int K, hipStream_t st) {
-    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, M, N,
-                       K);
+template <int DT, int BITS, int GS, int MT, int KS, int RG>
+static void qmv_go(int M, int N, int K, const uint32_t* w, const void* s, const void* b, const void* x,
+                   void* out, hipStream_t st) {
+    const dim3 grid((N + QMV_ROWS * RG - 1) / (QMV_ROWS * RG), (M + MT - 1) / MT);
+    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS, RG>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, M,
+                       N, K);
 }
 
 template <int DT, int BITS, int GS>
 static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          int M, int N, int K, hipStream_t st) {
     const int mt = qmv_mt_for(M);
-    const int ks = qmv_ksplit_for(M, N, K, BITS);
-    const dim3 grid((N + QMV_ROWS - 1) / QMV_ROWS, (M + mt - 1) / mt);
     if (mt == 1) {
-        if (ks == 4) qmv_go<DT, BITS, GS, 1, 4>(grid, w, s, b, x, out, M, N, K, st);
-        else if (ks == 2) qmv_go<DT, BITS, GS, 1, 2>(grid, w, s, b, x, out, M, N, K, st);
-        else qmv_go<DT, BITS, GS, 1, 1>(grid, w, s, b, x, out, M, N, K, st);
+        const QmvSplit sp = qmv_split_for(M, N, K, BITS);
+        switch (sp.ks * 8 + sp.rg) {
+            case 1 * 8 + 2: qmv_go<DT, BITS, GS, 1, 1, 2>(M, N, K, w, s, b, x, out, st); break;
+            case 1 * 8 + 4: qmv_go<DT, BITS, GS, 1, 1, 4>(M, N, K, w, s, b, x, out, st); break;
+            case 2 * 8 + 1: qmv_go<DT, BITS, GS, 1, 2, 1>(M, N, K, w, s, b, x, out, st); break;
+            case 4 * 8 + 1: qmv_go<DT, BITS, GS, 1, 4, 1>(M, N, K, w, s, b, x, out, st); break;
+            case 5 * 8 + 2: qmv_go<DT, BITS, GS, 1, 5, 2>(M, N, K, w, s, b, x, out, st); break;
+            case 5 * 8 + 4: qmv_go<DT, BITS, GS, 1, 5, 4>(M, N, K, w, s, b, x, out, st); break;
+            default: qmv_go<DT, BITS, GS, 1, 1, 1>(M, N, K, w, s, b, x, out, st); break;
+        }
     } else if (mt == 2) {
-        qmv_go<DT, BITS, GS, 2, 1>(grid, w, s, b, x, out, M, N, K, st);
+        qmv_go<DT, BITS, GS, 2, 1, 1>(M, N, K, w, s, b, x, out, st);
     } else {
-        qmv_go<DT, BITS, GS, 4, 1>(grid, w, s, b, x, out, M, N, K, st);
+        qmv_go<DT, BITS, GS, 4, 1, 1>(M, N, K, w, s, b, x, out, st);
     }
     return hipGetLastError();
 }

@@ -96,6 +96,16 @@ def test_qmv_small_m(orc, M):
     check_affine(orc, "qmv", M, 18, 512, 8, 32, qi.F32, seed=1150 + M)
 
 
+@pytest.mark.parametrize("N,K,bits,dt", [(67, 256, 4, qi.BF16), (8192, 256, 4, qi.F16), (16384, 256, 4, qi.BF16),
+                                          (67, 1536, 8, qi.F32), (67, 2560, 8, qi.BF16), (2048, 2560, 8, qi.F16),
+                                          (6000, 2560, 4, qi.BF16)])
+def test_qmv_work_splits(orc, N, K, bits, dt):
+    """Shapes for which the M = 1 split rule picks each of its work splits (waves
+    per row tile x row groups per wave: 1x1, 1x2, 1x4, 2x1, 4x1, 5x2, 5x4);
+    ragged N where the shape allows."""
+    check_affine(orc, "qmv", 1, N + (3 if N > 4000 else 0), K, bits, 64, dt, seed=1160 + N + K + bits)
+
+
 def test_qmv_config1_full(orc):
     # M=1, N=K=4096, 4-bit gs64, float32 everywhere (all outputs checked, reruns bit-identical)
     check_affine(orc, "qmv", 1, 4096, 4096, 4, 64, qi.F32, seed=qi.seed_for(1, 0), reruns=2)
@@ -222,7 +232,7 @@ def test_accumulate_sums_in_order_and_rounds_once(orc):
             assert np.array_equal(out64(out, dt), want)
 
 
-@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.F16)])
+@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.F16), (2, 128, qi.BF16)])
 def test_scale_bias_alignment_paths(orc, bits, gs, dt):
     """Scales/biases that start 2 bytes past a 16-byte boundary cannot be staged in
     16-byte chunks; the per-block path must give the same bits as the staged one."""
@@ -245,6 +255,18 @@ def test_scale_bias_alignment_paths(orc, bits, gs, dt):
         torch.cuda.synchronize()
         assert torch.equal(y_a.view(torch.int16), y_b.view(torch.int16)), route
         assert_close(out64(y_b, dt), orc.affine_case(c), dt, orc, what=f"{route} shifted scales")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_splitk_ragged_partitions(orc, bits, gs):
+    """bf16 partitions whose K ranges start and end inside a 16-byte chunk of
+    scales/biases (8 groups) and rows whose group count is not a multiple of 16;
+    M covers 1 to 6 row fragments."""
+    for M, N, K, S in ((9, 256, 3072, 5), (40, 384, 5120, 3), (85, 200, 7168, 7), (33, 130, 1536, 1)):
+        say("ragged partitions", M, N, K, bits, gs, S)
+        check_affine(orc, "splitk" if S > 1 else "qmm_t", M, N, K, bits, gs, qi.BF16,
+                     seed=2100 + bits * 10 + gs + M, **({"splits": S} if S > 1 else {}))
 
 
 def test_splitk_many_m_tiles(orc):
