@@ -101,7 +101,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="one of: " + ", ".join(sorted(WORKLOADS)) + ", or only:<call name>")
-    ap.add_argument("--reps", type=int, default=8, help="replays per per-call timing graph")
+    ap.add_argument("--reps", type=int, default=20, help="replays per per-call timing graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail-out", default=None, help="write per-call details as JSON here")
@@ -187,7 +187,7 @@ def per_call_us(c, sets, idx, reps):
     """Average µs per launch of call `idx`: a graph launches it once per rotating
     set; the graph is replayed `reps` times between two HIP events."""
     g = capture(lambda: [launch(c, s[idx]) for s in sets])
-    g.replay()
+    time_graphs([g], 3)   # warm-up: the GPU idles while the host captures
     _, ms = time_graphs([g], reps)
     return 1000.0 * ms / (reps * len(sets))
 
@@ -197,7 +197,7 @@ def per_kernel_us(fn, sets, idx, reps):
     set; the graph is replayed `reps` times between two HIP events on the
     stream the kernels run on."""
     g = capture(lambda: [fn(s[idx]) for s in sets])
-    g.replay()
+    time_graphs([g], 3)   # warm-up: the GPU idles while the host captures
     _, ms = time_graphs([g], reps)
     return 1000.0 * ms / (reps * len(sets))
 

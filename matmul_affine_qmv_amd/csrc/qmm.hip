@@ -16,7 +16,11 @@ int qmm_mt_for(int M) {
     return 8;
 }
 
-int qmm_mtiles_for(int M) { return M <= 128 ? 1 : (M + 127) / 128; }
+// Tiles of at most 64 rows up to M = 192 (MT <= 4: measured 15-20% faster per
+// call at M = 85 and 128 than one tile of 6 or 8 fragments, as the larger tiles
+// lose ring depth and staged scales to LDS); 128-row tiles beyond, where the
+// fewer, fuller tiles fill the chip better.
+int qmm_mtiles_for(int M) { return M <= 192 ? (M + 63) / 64 : (M + 127) / 128; }
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                         float* ws, int M, int N, int K, int bits, int gs, int dt, int splits,

@@ -161,7 +161,8 @@ def test_block_validation():
     (16, 4096, 4096, BF16, "qmm_t_splitk", 8),       # 32 tiles on 256 CUs
     (16, 4096, 256, BF16, "qmm_t", 1),               # K < 512 stays unsplit
     (22, 2048, 2048, BF16, "qmm_t_splitk", 8),       # capped at K / 256 partitions
-    (85, 2048, 10752, BF16, "qmm_t_splitk", 16),
+    (85, 2048, 10752, BF16, "qmm_t_splitk", 8),       # 2 M tiles of 43 rows x 16 N tiles
+    (128, 4096, 4096, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 N tiles
     (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
     (56, 5120, 17408, BF16, "qmm_t_splitk", 6),      # floor(256 / 40 tiles)
     (512, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 4 M tiles x 32 N tiles = 128 tiles
