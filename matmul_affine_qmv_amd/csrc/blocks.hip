@@ -72,12 +72,16 @@ __device__ __forceinline__ void blk_rounds(const float* __restrict__ x, int K, i
 }
 
 __device__ __forceinline__ void blk_store(float (&acc)[BLK_ROWS], int lane, int n0, int N, float* __restrict__ out) {
+    // the same fixed butterfly as wave_sum, step-major so the rows' exchanges of a
+    // step share one wait
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < BLK_ROWS; ++r) acc[r] += __shfl_xor(acc[r], off, 64);
     float mine = 0.f;
 #pragma unroll
-    for (int r = 0; r < BLK_ROWS; ++r) {
-        const float t = wave_sum(acc[r]);
-        if (lane == r) mine = t;
-    }
+    for (int r = 0; r < BLK_ROWS; ++r)
+        if (lane == r) mine = acc[r];
     if (lane < BLK_ROWS && n0 + lane < N) out[n0 + lane] = mine;
 }
 

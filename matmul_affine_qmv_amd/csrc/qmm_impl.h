@@ -465,22 +465,35 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     }
     stage_barrier<0>();
     if (wk == 1) return;
+    // every partner value is read before the first store, so the LDS reads share
+    // one wait instead of one each in front of every (row-predicated) store
 #pragma unroll
     for (int mf = 0; mf < MT; ++mf)
 #pragma unroll
         for (int nf = 0; nf < NB; ++nf)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float r = run[mf][nf][v] + red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane];
-                const int m = m0 + mf * 16 + 4 * lgrp + v;
-                const int n = n0 + wn * (NB * 16) + nf * 16 + lrow;
-                if (m < M && n < N) {
-                    if constexpr (SPLIT)
-                        ws[((size_t)split * M + m) * N + n] = r;
-                    else
-                        store_elem<DT>(out, (size_t)m * N + n, r);
+            for (int v = 0; v < 4; ++v) run[mf][nf][v] += red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane];
+    const int nl = n0 + wn * (NB * 16) + lrow;   // this lane's column in fragment 0
+    const bool cols_ok = n0 + QMM_BN <= N;
+#pragma unroll
+    for (int mf = 0; mf < MT; ++mf)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + mf * 16 + 4 * lgrp + v;
+            if (m < M) {
+                const size_t row = SPLIT ? ((size_t)split * M + m) * N : (size_t)m * N;
+#pragma unroll
+                for (int nf = 0; nf < NB; ++nf) {
+                    const int n = nl + nf * 16;
+                    if (cols_ok || n < N) {
+                        if constexpr (SPLIT)
+                            ws[row + n] = run[mf][nf][v];
+                        else
+                            store_elem<DT>(out, row + n, run[mf][nf][v]);
+                    }
                 }
             }
+        }
 }
 
 template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>

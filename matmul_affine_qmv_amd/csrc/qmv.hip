@@ -376,17 +376,20 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
         qmv_consume(a, acc);
     }
 
-    // sums over the LP lanes of each row group (fixed xor butterflies)
+    // sums over the LP lanes of each row group (fixed xor butterflies); the step
+    // loop is outermost so the R*MT independent exchanges of a step share a wait
+#pragma unroll
+    for (int off = LP / 2; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
     float mine = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            float tot = acc[r][m];
-#pragma unroll
-            for (int off = LP / 2; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
-            if (ll == r * MT + m) mine = tot;
-        }
+        for (int m = 0; m < MT; ++m)
+            if (ll == r * MT + m) mine = acc[r][m];
     if constexpr (KSPLIT > 1) {
         __shared__ float part[KSPLIT][RG * R * MT];
         if (ll < R * MT) part[wave][lp * R * MT + ll] = mine;
