@@ -418,26 +418,36 @@ struct QmvSplit {
     int ks, rg;
 };
 
-// Measured on the chip: a wave-round (one round of one wave, whatever its lane
-// use) costs about 1 us of a SIMD's time when the loads stream, and a wave's
-// rounds run one after another at about 1.6 us each when few waves are in
-// flight; each extra wave of a work-group adds its share of the cross-wave sum.
-// The split with the lowest max(wave-rounds per SIMD * 1 us, rounds * 1.6 us)
-// + 0.15 us * KS wins, the one with fewer rounds on ties.
+// Measured on the chip (sweeps of every split on the four 4-bit shapes with K =
+// 5120 or 14336): a wave-round (one round of one wave, whatever its lane use)
+// costs about 1 us of a SIMD's time when the loads stream, 10% more per extra
+// row group (its loads touch more rows at once); a wave's rounds run one after
+// another at about 1.6 us each when few waves are in flight; a launch of more
+// waves than stay resident (about 7 per SIMD) pays about 0.5 us per extra
+// generation.  When the rows alone give about 6 waves per SIMD, sharing a wave
+// between row groups measured slower, so only RG = 1 is considered.  The split
+// with the lowest max(wave-rounds per SIMD * (1 + 0.1 (RG - 1)) us, rounds *
+// 1.6 us) + 0.5 us * (generations - 1) wins; ties go to fewer rounds, then to
+// fewer waves per row tile.
 QmvSplit qmv_split_for(int M, int N, int K, int bits) {
     if (qmv_mt_for(M) != 1) return {1, 1};
     static constexpr QmvSplit kCands[] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {4, 1}, {5, 2}, {5, 4}};
+    constexpr long kResident = 7 * 1024;
     const long chunks = (long)K * bits / 128;
+    const bool rows_fill = (long)(N + QMV_ROWS - 1) / QMV_ROWS >= 6000;
     QmvSplit best = {1, 1};
     double best_t = -1.0;
     long best_rounds = 0;
     for (const QmvSplit& c : kCands) {
+        if (rows_fill && c.rg != 1) continue;
         const long per_wave = (chunks + c.ks - 1) / c.ks;
         if (c.ks > 1 && per_wave < 16) continue;
         const long lanes = 64 / c.rg;
         const long rounds = (per_wave + lanes - 1) / lanes;
         const long waves = (long)((N + QMV_ROWS * c.rg - 1) / (QMV_ROWS * c.rg)) * c.ks;
-        const double t = std::max((double)(waves * rounds) / 1024.0, 1.6 * (double)rounds) + 0.15 * c.ks;
+        const long gens = (waves + kResident - 1) / kResident;
+        const double t = std::max((double)(waves * rounds) / 1024.0 * (1.0 + 0.1 * (c.rg - 1)), 1.6 * (double)rounds) +
+                         0.5 * (double)(gens > 1 ? gens - 1 : 0);
         if (best_t < 0 || t < best_t - 1e-9 || (t < best_t + 1e-9 && rounds < best_rounds)) {
             best = c;
             best_t = t;
