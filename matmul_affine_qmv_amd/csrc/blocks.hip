@@ -18,6 +18,8 @@ constexpr int BLK_ROWS = 4;                         // output rows per wave
 constexpr int BLK_WAVES = 4;                        // waves per work-group
 constexpr int BLK_THREADS = 64 * BLK_WAVES;
 constexpr int BLK_ROUND = 2048;                     // x values per round (8 KB)
+constexpr int BLK_XPT = BLK_ROUND / 4 / BLK_THREADS;   // 16-byte x pieces per thread per round
+static_assert(BLK_XPT >= 1 && BLK_XPT * BLK_THREADS * 4 == BLK_ROUND, "x round split");
 
 // The round's x as 512 16-byte pieces.  Piece u (x values 4u..4u+3 of the
 // round) is stored at slot u ^ ((u >> 4) & 15), which spreads the pieces the
@@ -25,18 +27,19 @@ constexpr int BLK_ROUND = 2048;                     // x values per round (8 KB)
 __device__ __forceinline__ int x_slot(int u) { return u ^ ((u >> 4) & 15); }
 
 // Load the round starting at x value k0 (clamped into [0, K)): thread t takes
-// pieces 2t and 2t+1.
-__device__ __forceinline__ void x_round_load(const float* __restrict__ x, int K, int k0, int tid, u32x4 (&v)[2]) {
+// pieces BLK_XPT*t .. BLK_XPT*t + BLK_XPT - 1.
+__device__ __forceinline__ void x_round_load(const float* __restrict__ x, int K, int k0, int tid,
+                                             u32x4 (&v)[BLK_XPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = min(k0 + 4 * (2 * tid + j), K - 4);
+    for (int j = 0; j < BLK_XPT; ++j) {
+        const int e = min(k0 + 4 * (BLK_XPT * tid + j), K - 4);
         v[j] = *reinterpret_cast<const u32x4*>(x + e);
     }
 }
 
-__device__ __forceinline__ void x_round_store(u32x4* buf, int tid, const u32x4 (&v)[2]) {
+__device__ __forceinline__ void x_round_store(u32x4* buf, int tid, const u32x4 (&v)[BLK_XPT]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) buf[x_slot(2 * tid + j)] = v[j];
+    for (int j = 0; j < BLK_XPT; ++j) buf[x_slot(BLK_XPT * tid + j)] = v[j];
 }
 
 __device__ __forceinline__ void x_piece(const u32x4* buf, int u, float* dst) {
@@ -53,7 +56,7 @@ __device__ __forceinline__ void x_piece(const u32x4* buf, int u, float* dst) {
 template <typename WStage, typename Load, typename Consume>
 __device__ __forceinline__ void blk_rounds(const float* __restrict__ x, int K, int rounds, int tid,
                                            u32x4 (*xl)[BLK_ROUND / 4], Load&& load, Consume&& consume) {
-    u32x4 v[2];
+    u32x4 v[BLK_XPT];
     WStage cur, nxt;
     load(0, cur);
     x_round_load(x, K, 0, tid, v);
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __res
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
     const int nb = K / 32;
-    float acc[BLK_ROWS] = {0.f, 0.f, 0.f, 0.f};
+    float acc[BLK_ROWS] = {};
 
     struct WS { uint32_t w[BLK_ROWS][9]; };
     if (nb > 0) {
@@ -143,16 +146,30 @@ __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __res
 // 64g+32+i of sub-block 2g+1.  Per sub-block part the sum of q*x and the sum
 // of x are formed once; the weight d*sc*q - dmin*m is applied as
 // d*sc*sum(q x) - dmin*m*sum(x).
-__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
+// The 6-bit scale and min of sub-block j from the scale words s0, s1, s2
+// (bytes 0-3, 4-7, 8-11).  Both are a 4-bit field plus a 2-bit field above it:
+// j < 4: sc = s0 bits [8j, 8j+4) | s0 bits [8j+4, 8j+6) << 4,
+//        mn = s1 bits [8j, 8j+4) | s1 bits [8j+4, 8j+6) << 4;
+// j >= 4 (jj = j - 4): sc = s2 bits [8jj, 8jj+4) | s0 bits [8jj+6, 8jj+8) << 4,
+//        mn = s2 bits [8jj+4, 8jj+8) | s1 bits [8jj+6, 8jj+8) << 4.
+// The word and bit positions depend only on j, so a lane forms them once.
+struct Q4kFields {
+    bool hi;               // j >= 4: the low 4 bits come from s2
+    uint32_t sc_lo, mn_lo;  // positions of the 4-bit fields
+    uint32_t sc_up, mn_up;  // positions of the 2-bit fields (in s0 and s1)
+};
+
+__device__ __forceinline__ Q4kFields q4k_fields(int j) {
+    const uint32_t jj = (uint32_t)(j & 3);
+    if (j < 4) return {false, 8 * jj, 8 * jj, 8 * jj + 4, 8 * jj + 4};
+    return {true, 8 * jj, 8 * jj + 4, 8 * jj + 6, 8 * jj + 6};
+}
+
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, const Q4kFields& f,
                                               uint32_t& sc, uint32_t& mn) {
-    // s0, s1, s2: scale bytes 0-3, 4-7, 8-11.
-    const int jj = j & 3;
-    const uint32_t lo_sc = (s0 >> (8 * jj)) & 63u;
-    const uint32_t lo_mn = (s1 >> (8 * jj)) & 63u;
-    const uint32_t hi_sc = ((s2 >> (8 * jj)) & 15u) | (((s0 >> (8 * jj + 6)) & 3u) << 4);
-    const uint32_t hi_mn = ((s2 >> (8 * jj + 4)) & 15u) | (((s1 >> (8 * jj + 6)) & 3u) << 4);
-    sc = j < 4 ? lo_sc : hi_sc;
-    mn = j < 4 ? lo_mn : hi_mn;
+    const uint32_t a = f.hi ? s2 : s0, c = f.hi ? s2 : s1;
+    sc = __builtin_amdgcn_ubfe(a, f.sc_lo, 4) | (__builtin_amdgcn_ubfe(s0, f.sc_up, 2) << 4);
+    mn = __builtin_amdgcn_ubfe(c, f.mn_lo, 4) | (__builtin_amdgcn_ubfe(s1, f.mn_up, 2) << 4);
 }
 
 __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __restrict__ wb,
@@ -164,7 +181,8 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
     const int g = part >> 1, t0 = (part & 1) * 16;
     const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
     const int nb = K / 256;
-    float acc[BLK_ROWS] = {0.f, 0.f, 0.f, 0.f};
+    const Q4kFields f_lo = q4k_fields(2 * g), f_hi = q4k_fields(2 * g + 1);
+    float acc[BLK_ROWS] = {};
 
     struct WS { u32x4 hdr[BLK_ROWS], qw[BLK_ROWS]; };
     if (nb > 0) {
@@ -194,13 +212,16 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
                 const float d = f16_bits_to_f32(st.hdr[r].x & 0xffffu);
                 const float dmin = f16_bits_to_f32(st.hdr[r].x >> 16);
                 uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
-                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, 2 * g, sc_lo, mn_lo);
-                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, 2 * g + 1, sc_hi, mn_hi);
+                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, f_lo, sc_lo, mn_lo);
+                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, f_hi, sc_hi, mn_hi);
                 float sl = 0.f, sh = 0.f;
                 const uint32_t qws[4] = {st.qw[r].x, st.qw[r].y, st.qw[r].z, st.qw[r].w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
+                    uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
+                    // keep the masked words whole so each code converts with one
+                    // byte-select v_cvt_f32_ubyte<i> instead of a field extract plus a convert
+                    asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         sl = fmaf((float)((lo >> (8 * i)) & 0xffu), xlo[4 * k + i], sl);
