@@ -51,26 +51,30 @@ __device__ __forceinline__ void x_piece(const u32x4* buf, int u, float* dst) {
 }
 
 // Per-round skeleton shared by both formats: while round r is consumed, the
-// weights of round r + 1 are already requested into registers and its x is
-// loaded, then staged into the other LDS buffer; one barrier per round.
+// weights of round r + 1 are already requested into the other register set and
+// its x is loaded, then staged into the other LDS buffer; one barrier per round.
 template <typename WStage, typename Load, typename Consume>
 __device__ __forceinline__ void blk_rounds(const float* __restrict__ x, int K, int rounds, int tid,
                                            u32x4 (*xl)[BLK_ROUND / 4], Load&& load, Consume&& consume) {
     u32x4 v[BLK_XPT];
-    WStage cur, nxt;
-    load(0, cur);
+    WStage a, b;
+    load(0, a);
     x_round_load(x, K, 0, tid, v);
     x_round_store(xl[0], tid, v);
     __syncthreads();
-    for (int rd = 0; rd < rounds; ++rd) {
-        // past the last round the loads repeat the last round and are never used
+    // past the last round the loads repeat the last round and are never used
+    auto step = [&](int rd, const WStage& cur, WStage& nxt) {
         const int rn = min(rd + 1, rounds - 1);
         load(rn, nxt);
         x_round_load(x, K, rn * BLK_ROUND, tid, v);
         consume(xl[rd & 1], rd, cur);
         x_round_store(xl[(rd + 1) & 1], tid, v);
         __syncthreads();
-        cur = nxt;
+    };
+    // two rounds per trip, alternating the register sets, so no set is copied
+    for (int rd = 0; rd < rounds; rd += 2) {
+        step(rd, a, b);
+        if (rd + 1 < rounds) step(rd + 1, b, a);
     }
 }
 
