@@ -95,13 +95,16 @@ int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases,
             int dtype, void* stream);
 
 /* qmx_qmm_t -- affine quantized x * W^T for M >= 8 on the matrix cores
- * (page "mlx PR 4682": staged transposed qmm with register prefetch, a
- * double-buffered threadgroup-memory stage and one barrier per K step).
- * Packed codes, x, scales and biases of the next K block are prefetched
- * into registers while the matrix cores consume the current LDS buffer;
- * the codes are expanded to exact 16-bit integers right before bf16/f16
- * MFMA, and scale and bias are applied per group in float32, so the only
- * rounding besides float32 accumulation is the final one.
+ * (page "mlx PR 4682": staged transposed qmm that fetches the next K step
+ * while the current one is consumed from threadgroup memory, with one
+ * barrier per K step).  Here the packed codes and x of the next K blocks are
+ * copied from HBM straight into a ring of LDS stages (global-to-LDS loads,
+ * no register staging) while the matrix cores consume the current stage;
+ * scales and biases are staged once per work-group in 16-byte chunks when
+ * aligned, else with each stage.  Codes are expanded to exact 16-bit values
+ * right before bf16/f16 MFMA, and scale and bias are applied per group in
+ * float32, so the only rounding besides float32 accumulation is the final
+ * one.
  * dtype: QMX_F16 or QMX_BF16 only (QMX_ERR_DTYPE for QMX_F32).
  * Extra requirements: K % 128 == 0; w_packed, x 16-byte aligned.
  */

@@ -7,12 +7,16 @@
 // accumulators, and a cross-lane reduction followed by one store per output.
 //
 // gfx950 mapping:
-// * A wave owns QMV_ROWS consecutive rows of W and up to MT rows of x, and
-//   a contiguous range of the row's 16-byte chunks; lane l takes chunks
-//   l, l+64, ... of that range, so each wave-wide load reads 1 KB of one row.
-//   When N alone gives too few waves to cover the chip, KSPLIT waves of one
-//   work-group split the chunks of the same rows and their partial sums are
-//   added in LDS in a fixed order.
+// * A row group is QMV_ROWS consecutive rows of W, served with up to MT rows
+//   of x.  A wave owns RG row groups (64/RG lanes each) and a contiguous range
+//   of their 16-byte chunks; lane l of a row group takes chunks l, l + 64/RG,
+//   ... of that range, so each load instruction reads 256 B-1 KB contiguous
+//   per row.  KSPLIT waves of one work-group may split the chunks of the same
+//   rows; their partial sums are added in LDS in a fixed order.  The split
+//   (KSPLIT, RG) comes from qmv_split_for.
+// * Loads are buffer loads through resources based at the work-group's first
+//   row; per-lane offsets are fixed for the loop and each round adds one
+//   scalar offset, so the loop does no address arithmetic on the vector ALU.
 // * 16-bit x: a word is split into byte-aligned fields and one v_perm per
 //   pair of codes sets a magic exponent byte above two of them (0x43qq is the
 //   bf16 value 128+q, 0x64qq the f16 value 1024+q; f16 then subtracts 1024
@@ -367,9 +371,9 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
 
-    // One chunk in flight per wave: the register budget goes to occupancy
-    // (6-7 waves per SIMD), which overlaps loads and arithmetic better on
-    // this kernel than a second register set at half the occupancy.
+    // One chunk round in flight per wave: the register budget goes to
+    // occupancy (about 7 waves per SIMD), which overlaps loads and arithmetic
+    // better on this kernel than a second register set at lower occupancy.
     for (int round = 0; c < c1; c += LP, ++round) {
         S a;
         qmv_load(a, ad, round * STEP_W, round * STEP_SB, round * STEP_X);
