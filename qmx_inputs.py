@@ -13,7 +13,9 @@ Q4_K block comments):
   bit stream, element ``k`` occupies bits ``[k*bits, (k+1)*bits)`` of the row
   stream, so for 4-bit codes element ``i`` sits at bits ``4*(i%8)`` of word
   ``i//8`` (low nibble first) and for 8-bit codes byte ``j`` of a word holds
-  element ``4*word + j``.
+  element ``4*word + j``.  The same stream carries the other widths the
+  staged loader of page "mlx PR 4682" takes (1, 3, 5 and 6 bits); 3-, 5- and
+  6-bit fields may straddle two words.
 * Q8_0: 9 uint32 per 32-weight block; word 0 holds the f16 scale in its low
   16 bits (high half zero), words 1..8 hold the 32 signed int8 quants, four
   per word, quant ``i`` at byte ``i%4`` of word ``1 + i//4``.
@@ -28,6 +30,8 @@ and rounded round-to-nearest-even to the storage dtype.  Draw order: codes,
 scales, bias jitter, x.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -81,16 +85,31 @@ def storage_to_f64(a, dt) -> np.ndarray:
 
 # ---------------------------------------------------------------- layouts
 def pack_codes(codes, bits: int) -> np.ndarray:
-    """Pack unsigned codes ``[N, K]`` into row bit streams of uint32 words."""
+    """Pack unsigned codes ``[N, K]`` into row bit streams of uint32 words:
+    element k at stream bits [k*bits, (k+1)*bits), word 0 holding stream bits
+    0..31, so 3-, 5- and 6-bit fields may straddle two words."""
     codes = np.asarray(codes)
     n, k = codes.shape
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be 1..8")
     if (k * bits) % 32:
         raise ValueError("K*bits must be a multiple of 32")
-    per = 32 // bits
-    out = np.zeros((n, k // per), dtype=np.uint32)
-    for j in range(per):
-        out |= codes[:, j::per].astype(np.uint32) << np.uint32(bits * j)
-    return out
+    if 32 % bits == 0:
+        per = 32 // bits
+        out = np.zeros((n, k // per), dtype=np.uint32)
+        for j in range(per):
+            out |= codes[:, j::per].astype(np.uint32) << np.uint32(bits * j)
+        return out
+    # a period of P codes fills exactly P*bits/32 words; place element i of every period
+    P = 32 // math.gcd(32, bits)
+    out = np.zeros((n, k // P, P * bits // 32), dtype=np.uint64)
+    for i in range(P):
+        bit = i * bits
+        v = codes[:, i::P].astype(np.uint64) << np.uint64(bit & 31)
+        out[:, :, bit >> 5] |= v & np.uint64(0xFFFFFFFF)
+        if (bit & 31) + bits > 32:
+            out[:, :, (bit >> 5) + 1] |= v >> np.uint64(32)
+    return out.reshape(n, k * bits // 32).astype(np.uint32)
 
 
 def random_codes(rng, shape, bits: int) -> np.ndarray:

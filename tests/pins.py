@@ -137,9 +137,9 @@ def _rel_err(got, exact_fracs):
 def pin_affine_brute(o):
     shapes = [(1, 1, 32, 32), (2, 3, 64, 32), (3, 2, 256, 64), (1, 8, 512, 128), (2, 2, 128, 128)]
     case_id = 0
-    for bits in (2, 4, 8):
+    for bits in (1, 2, 3, 4, 5, 6, 8):
         for dt in (F32, F16, BF16):
-            for (M, N, K, gs) in shapes:
+            for (M, N, K, gs) in (shapes if bits in (2, 4, 8) else shapes[:3]):
                 if (K * bits) % 32:
                     continue
                 case_id += 1
@@ -170,7 +170,9 @@ def pin_q4_k_brute(o):
 def pin_dense_numpy(o):
     """Dequantise from the raw codes with numpy, then x @ W.T in float64."""
     for i, (M, N, K, bits, gs, dt) in enumerate([(3, 16, 1024, 4, 64, BF16), (2, 9, 512, 2, 32, F16),
-                                                (4, 7, 384, 8, 128, F32), (1, 33, 4096, 4, 64, F32)]):
+                                                (4, 7, 384, 8, 128, F32), (1, 33, 4096, 4, 64, F32),
+                                                (2, 5, 384, 3, 64, BF16), (3, 6, 256, 5, 32, F16),
+                                                (1, 7, 192, 6, 64, F32), (2, 4, 256, 1, 128, BF16)]):
         c = qi.affine_case(M, N, K, bits, gs, dt, seed=970 + i)
         W = dense_weights(c)
         X = qi.storage_to_f64(c["x"], dt)

@@ -16,6 +16,7 @@ MUTANTS = {
                      ";\n            acc += value_at(x, x_dt"),
     "nibble_order_reversed": ("return (unsigned)((window >> sh) & ((1u << bits) - 1u));",
                               "return (unsigned)((window >> (32 - bits - sh)) & ((1u << bits) - 1u));"),
+    "straddling_field_truncated": ("if (sh + bits > 32) window |= (uint64_t)row[wi + 1] << 32;", ""),
     "wrong_group_index": ("long g = k / gs;", "long g = (k + 1) / gs; if (g >= G) g = G - 1;"),
     "x_index_transposed": ("acc += value_at(x, x_dt, (size_t)m * K + k) * wk;",
                            "acc += value_at(x, x_dt, (size_t)k * M + m) * wk;"),
