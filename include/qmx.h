@@ -29,14 +29,15 @@
  *   w_packed : uint32 [N, K*bits/32]; row n is a little-endian bit stream,
  *              code q[n,k] is the unsigned field at stream bits
  *              [k*bits, (k+1)*bits) (4-bit: 8 codes per word, low nibble
- *              first; 8-bit: byte j of a word is code 4*word+j).
+ *              first; 8-bit: byte j of a word is code 4*word+j; 3-, 5- and
+ *              6-bit fields may straddle two words).
  *   scales, biases : [N, K/group_size] in `dtype`.
  *   x        : [M, K] in `dtype`.     out : [M, N] in `dtype`.
  *   out[m,n] = sum_g ( scales[n,g] * sum_{k in g} q[n,k] * x[m,k]
  *                    + biases[n,g] * sum_{k in g} x[m,k] )
  *            = sum_k x[m,k] * (scales[n,k/gs] * q[n,k] + biases[n,k/gs]).
- * Supported: bits in {2, 4, 8}; group_size in {32, 64, 128};
- * K % group_size == 0.
+ * Supported: bits in {1, 2, 3, 4, 5, 6, 8} (the widths of the staged loader
+ * of page "mlx PR 4682"); group_size in {32, 64, 128}; K % group_size == 0.
  */
 #ifndef QMX_H
 #define QMX_H
@@ -60,7 +61,7 @@ typedef enum qmx_status {
     QMX_OK = 0,
     QMX_ERR_NULL = -1,       /* a required pointer is NULL                        */
     QMX_ERR_SHAPE = -2,      /* negative size, or a size the route cannot take     */
-    QMX_ERR_BITS = -3,       /* bits not in {2, 4, 8}                              */
+    QMX_ERR_BITS = -3,       /* bits not in {1, 2, 3, 4, 5, 6, 8}                  */
     QMX_ERR_GROUP = -4,      /* group_size not in {32, 64, 128} or K % gs != 0     */
     QMX_ERR_DTYPE = -5,      /* unknown dtype, or a dtype the route does not take  */
     QMX_ERR_ALIGN = -6,      /* a pointer lacks the alignment the route needs      */
@@ -81,14 +82,16 @@ typedef enum qmx_route {
 
 /* qmx_qmv -- affine quantized matvec for small M (built for M = 1..7).
  * Computes the affine definition above with float32 accumulation on the
- * vector ALUs: weight codes are streamed once with 16-byte loads, the sum
+ * vector ALUs: weight codes are streamed once in chunks of 16 bytes (2-, 4-
+ * and 8-bit) or of `bits` words = 32 codes (1, 3, 5, 6 bits), the sum
  * of x is formed once per group (bias hoist), lanes are reduced with a
  * fixed-order cross-lane tree (page "metaltile-std src/mlx/quantized.rs",
  * qmv kernel: bias hoist, x reuse across rows, simd_sum and lane-0 store).
  * dtype: QMX_F32, QMX_F16 or QMX_BF16 for x, scales, biases and out.
  * Any M >= 0 is accepted (rows of x are processed in tiles of up to 4).
- * Extra requirements: (K*bits) % 128 == 0 (rows of w_packed are whole
- * 16-byte chunks), w_packed 16-byte aligned, x aligned to its element size.
+ * Extra requirements: rows of w_packed are whole chunks ((K*bits) % 128 == 0
+ * for 2, 4 and 8 bits; K % 32 == 0, always true, for the others), w_packed
+ * 16-byte aligned, x aligned to its element size.
  */
 int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases,
             const void* x, void* out, int M, int N, int K, int bits, int group_size,

@@ -26,8 +26,12 @@ hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const v
                         float* ws, int M, int N, int K, int bits, int gs, int dt, int splits,
                         hipStream_t st) {
     switch (bits) {
+        case 1: return qmm_launch_b1(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
         case 2: return qmm_launch_b2(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+        case 3: return qmm_launch_b3(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
         case 4: return qmm_launch_b4(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+        case 5: return qmm_launch_b5(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+        case 6: return qmm_launch_b6(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
         default: return qmm_launch_b8(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
     }
 }

@@ -1,5 +1,5 @@
 // qmm_b2.hip -- 2-bit instances of the staged qmm_t kernel (kept apart so the
-// three code widths compile in parallel).
+// code widths compile in parallel).
 #include "qmm_impl.h"
 
 namespace qmx {

@@ -1,0 +1,12 @@
+// qmm_b3.hip -- 3-bit instances of the staged qmm_t kernel (kept apart so the
+// code widths compile in parallel).
+#include "qmm_impl.h"
+
+namespace qmx {
+
+hipError_t qmm_launch_b3(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                         float* ws, int M, int N, int K, int gs, int dt, int splits, hipStream_t st) {
+    return qmm_launch_bits<3>(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+}
+
+}  // namespace qmx

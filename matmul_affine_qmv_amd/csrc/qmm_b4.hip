@@ -1,5 +1,5 @@
 // qmm_b4.hip -- 4-bit instances of the staged qmm_t kernel (kept apart so the
-// three code widths compile in parallel).
+// code widths compile in parallel).
 #include "qmm_impl.h"
 
 namespace qmx {

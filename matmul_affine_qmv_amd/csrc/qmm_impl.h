@@ -53,11 +53,14 @@ struct QmmCfg {
     static constexpr int XPT = (BM + 31) / 32;                // x copies per thread per block
     static constexpr int XROWS = 32 * XPT;
     static constexpr int X_BYTES = XROWS * 256;
-    // W: 16*BITS bytes per row per block.  2-bit rows are copied 4 bytes per
-    // lane (two copies per thread), wider ones 16 bytes per lane.
+    // W: 16*BITS bytes per row per block.  4- and 8-bit rows are copied 16
+    // bytes per lane; 2-bit rows and the widths that do not divide 32 (1, 3,
+    // 5, 6: BITS words of 32 codes, fields straddling words) 4 bytes per lane.
+    static constexpr bool ODD = !(BITS == 2 || BITS == 4 || BITS == 8);
+    static constexpr bool W4B = BITS == 2 || ODD;             // 4-byte W copies
     static constexpr int W_ROW = 16 * BITS;
     static constexpr int W_BYTES = QMM_BN * W_ROW;
-    static constexpr int WPT = BITS == 4 ? 1 : 2;             // W copies per thread per block
+    static constexpr int WPT = BITS == 4 ? 1 : ODD ? BITS : 2; // W copies per thread per block
     // Scales then biases.  Staged per block, one 16-bit value per lane
     // (zero-extended to 4 bytes in LDS), unless SBV: then the work-group's whole
     // K range of both is copied once, before the ring, in 16-byte chunks.
@@ -83,6 +86,7 @@ struct QmmCfg {
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
     static_assert(STAGE % 1024 == 0 && X_BYTES % 1024 == 0, "stage alignment");
+    static_assert(WPT * QMM_THREADS * (W4B ? 4 : 16) == W_BYTES, "whole W copies per thread");
     static_assert(!SBV || SBV_CHUNKS >= 3, "room for the staged scales and biases");
 };
 
@@ -151,6 +155,34 @@ __device__ __forceinline__ u32x4 expand4(uint32_t w) {
     constexpr uint32_t MB = DT == DT_F16 ? 0x64646464u : 0x43434343u;
     return finish<DT>(u32x4{__builtin_amdgcn_perm(MB, c0123, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c0123, perm_sel(2, 3)),
                             __builtin_amdgcn_perm(MB, c4567, perm_sel(0, 1)), __builtin_amdgcn_perm(MB, c4567, perm_sel(2, 3))});
+}
+
+// 8 consecutive codes of a 1-, 3-, 5- or 6-bit stream: they fill exactly BITS
+// bytes, starting at byte sh (0..3) of word lo (hi the next word).  One byte
+// shift brings them to bit 0; each pair is cut as one 2*BITS-bit window t,
+// and t | t << (16 - BITS) puts its second code at bit 16 under the magic
+// bytes.
+template <int DT, int BITS>
+__device__ __forceinline__ u32x4 expand_stream(uint32_t lo, uint32_t hi, int sh) {
+    constexpr uint32_t MB = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    constexpr uint32_t MASK = (1u << BITS) - 1u, WIN = (1u << (2 * BITS)) - 1u;
+    uint32_t p[4];
+    if constexpr (8 * BITS <= 32) {
+        const uint32_t u = __builtin_amdgcn_alignbyte(hi, lo, sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = (u >> (2 * BITS * j)) & WIN;
+            p[j] = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
+        }
+    } else {
+        const uint64_t v = ((((uint64_t)hi) << 32) | lo) >> (8 * sh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = (uint32_t)(v >> (2 * BITS * j)) & WIN;
+            p[j] = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
+        }
+    }
+    return finish<DT>(u32x4{p[0], p[1], p[2], p[3]});
 }
 
 // 8 consecutive 2-bit codes held in the low 16 bits of h (code i at bits 2i).
@@ -247,7 +279,12 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
     for (int j = 0; j < C::WPT; ++j) {
         int R, q;
-        if constexpr (BITS == 4) {
+        if constexpr (C::ODD) {
+            // word v = 512j + tid of the block, row-major [R][4*BITS] in LDS
+            const int v = QMM_THREADS * j + tid;
+            R = v / (4 * BITS);
+            q = v % (4 * BITS);
+        } else if constexpr (BITS == 4) {
             R = 16 * wave + (lane >> 2);
             q = 4 * ((lane & 3) ^ ((R >> 2) & 3));
         } else if constexpr (BITS == 8) {
@@ -292,7 +329,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int i = 0; i < C::XPT; ++i) dma<16>(xsrc[i] + (size_t)kb * QMM_KB, X + (8 * i + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < C::WPT; ++j) {
-            if constexpr (BITS == 2)
+            if constexpr (C::W4B)
                 dma<4>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 256);
             else
                 dma<16>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 1024);
@@ -331,7 +368,14 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     const int c = kchunk<BITS, GS>(2 * wk + st, lgrp);
-                    if constexpr (BITS == 4) {
+                    if constexpr (C::ODD) {
+                        // chunk c's 8 codes are bytes [BITS*c, BITS*c + BITS) of the row's
+                        // block; the word after them may lie past the row (BITS = 1, 3), but
+                        // stays inside the LDS allocation and is then not used
+                        const int o = BITS * c;
+                        const uint32_t* rw = reinterpret_cast<const uint32_t*>(Wl + R * C::W_ROW);
+                        bf[st][nf] = expand_stream<DT, BITS>(rw[o >> 2], BITS > 1 ? rw[(o >> 2) + 1] : 0u, o & 3);
+                    } else if constexpr (BITS == 4) {
                         const uint32_t word = *reinterpret_cast<const uint32_t*>(
                             Wl + R * C::W_ROW + (((c >> 2) ^ ((R >> 2) & 3)) << 4) + 4 * (c & 3));
                         bf[st][nf] = expand4<DT>(word);
@@ -559,9 +603,17 @@ hipError_t qmm_launch_bits(const uint32_t* w, const void* s, const void* b, cons
     }
 }
 
+hipError_t qmm_launch_b1(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
+                         int, int, int, int, hipStream_t);
 hipError_t qmm_launch_b2(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
                          int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b3(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
+                         int, int, int, int, hipStream_t);
 hipError_t qmm_launch_b4(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
+                         int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b5(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
+                         int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b6(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
                          int, int, int, int, hipStream_t);
 hipError_t qmm_launch_b8(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
                          int, int, int, int, hipStream_t);

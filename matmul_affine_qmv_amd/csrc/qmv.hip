@@ -136,15 +136,17 @@ __device__ __forceinline__ void unpack_word(uint32_t w, float (&q)[32 / BITS]) {
     }
 }
 
-// Registers of one chunk: the R rows' 16-byte weight chunks, their scales and
-// biases (raw storage bits), and the MT rows' x values under the chunk.
+// Registers of one chunk: the R rows' weight chunks (CW words each), their
+// scales and biases (raw storage bits), and the MT rows' x values under the
+// chunk.
 template <int DT, int BITS, int GS, int MT>
 struct QmvStage {
     static constexpr int R = QMV_ROWS;
-    static constexpr int CPC = 128 / BITS;
+    static constexpr int CW = qmv_chunk_words(BITS);
+    static constexpr int CPC = qmv_chunk_codes(BITS);
     static constexpr int PARTS = CPC > GS ? CPC / GS : 1;
     static constexpr int XQ = CPC * (DT == DT_F32 ? 4 : 2) / 16;   // 16-byte x pieces per chunk
-    u32x4 w[R];
+    uint32_t w[R][CW];
     uint32_t s[R][PARTS], b[R][PARTS];
     u32x4 x[MT][XQ];
 };
@@ -188,8 +190,23 @@ __device__ __forceinline__ void qmv_load(QmvStage<DT, BITS, GS, MT>& st, const Q
         for (int i = 0; i < S::XQ; ++i)
             st.x[m][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.x, ad.vx[m] + 16 * i, sx, 0));
 #pragma unroll
-    for (int r = 0; r < S::R; ++r)
-        st.w[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ad.w, ad.vw[r], sw, 0));
+    for (int r = 0; r < S::R; ++r) {
+        if constexpr (S::CW == 1) {
+            st.w[r][0] = __builtin_amdgcn_raw_buffer_load_b32(ad.w, ad.vw[r], sw, 0);
+        } else if constexpr (S::CW == 3) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(ad.w, ad.vw[r], sw, 0);
+            st.w[r][0] = v[0]; st.w[r][1] = v[1]; st.w[r][2] = v[2];
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(ad.w, ad.vw[r], sw, 0);
+            st.w[r][0] = v[0]; st.w[r][1] = v[1]; st.w[r][2] = v[2]; st.w[r][3] = v[3];
+            if constexpr (S::CW == 5) {
+                st.w[r][4] = __builtin_amdgcn_raw_buffer_load_b32(ad.w, ad.vw[r] + 16, sw, 0);
+            } else if constexpr (S::CW == 6) {
+                const auto u = __builtin_amdgcn_raw_buffer_load_b64(ad.w, ad.vw[r] + 16, sw, 0);
+                st.w[r][4] = u[0]; st.w[r][5] = u[1];
+            }
+        }
+    }
 #pragma unroll
     for (int r = 0; r < S::R; ++r)
 #pragma unroll
@@ -206,9 +223,40 @@ __device__ __forceinline__ float raw_to_f32(uint32_t v) {
     else return bf16_bits_to_f32(v);
 }
 
-// Word j (0..3) of a 16-byte chunk.
+// Word j (0..3) of a 16-byte piece.
 __device__ __forceinline__ uint32_t word_of(const u32x4& v, int j) {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Code e of a chunk of CW words that holds its codes as one little-endian
+// bit stream (e and so the bit position are compile-time constants after
+// unrolling: one bit-field extract, or a funnel shift where the field
+// straddles two words).
+template <int BITS, int CW>
+__device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[CW], int e) {
+    const int bit = BITS * e, i = bit >> 5, sh = bit & 31;
+    constexpr uint32_t MASK = (1u << BITS) - 1u;
+    if (sh + BITS <= 32) return (w[i] >> sh) & MASK;
+    return __builtin_amdgcn_alignbit(w[i + 1], w[i], sh) & MASK;
+}
+
+// Codes e and e + 1 of such a chunk as a pair of exact 16-bit values under
+// the magic exponent (128 + q in bf16, q in f16 after removing 1024).
+// The two fields are taken as one 2*BITS-bit window t (code e in its low
+// BITS bits); t | t << (16 - BITS) puts code e + 1 at bit 16, and one mask
+// keeps both codes under the magic bytes.
+template <int DT, int BITS, int CW>
+__device__ __forceinline__ uint32_t stream_pair(const uint32_t (&w)[CW], int e) {
+    constexpr uint32_t MB = DT == DT_BF16 ? 0x43004300u : 0x64006400u;
+    constexpr uint32_t MASK = (1u << BITS) - 1u, WIN = (1u << (2 * BITS)) - 1u;
+    const int bit = BITS * e, i = bit >> 5, sh = bit & 31;
+    const uint32_t t = (sh + 2 * BITS <= 32 ? w[i] >> sh : __builtin_amdgcn_alignbit(w[i + 1], w[i], sh)) & WIN;
+    uint32_t p = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
+    if constexpr (DT == DT_F16) {
+        const h2_t v = __builtin_bit_cast(h2_t, p) - h2_t{(_Float16)1024.f, (_Float16)1024.f};
+        p = __builtin_bit_cast(uint32_t, v);
+    }
+    return p;
 }
 
 template <int DT, int BITS, int GS, int MT>
@@ -231,7 +279,57 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
             for (int r = 0; r < R; ++r) qd[r][m][p] = 0.f;
         }
 
-    if constexpr (use_dot2<DT, BITS>()) {
+    if constexpr (S::CW != 4) {
+        // 1-, 3-, 5- and 6-bit codes: 32 per chunk in natural order, so codes
+        // 2k and 2k+1 pair with x dword k as it is loaded.
+        static_assert(PARTS == 1 && S::CPC == 32, "one group part of 32 codes per chunk");
+        if constexpr (DT != DT_F32) {
+            constexpr uint32_t ONES = DT == DT_BF16 ? 0x3f803f80u : 0x3c003c00u;
+            uint32_t xp[MT][16];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < S::XQ; ++i) {
+                    xp[m][4 * i] = st.x[m][i].x; xp[m][4 * i + 1] = st.x[m][i].y;
+                    xp[m][4 * i + 2] = st.x[m][i].z; xp[m][4 * i + 3] = st.x[m][i].w;
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) t = dot2<DT>(xp[m][k], ONES, t);
+                xs[m][0] = t;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const uint32_t q = stream_pair<DT, BITS>(st.w[r], 2 * k);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) qd[r][m][0] = dot2<DT>(q, xp[m][k], qd[r][m][0]);
+                }
+        } else {
+            float xv[MT][32];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < S::XQ; ++i) {
+                    xv[m][4 * i] = __uint_as_float(st.x[m][i].x); xv[m][4 * i + 1] = __uint_as_float(st.x[m][i].y);
+                    xv[m][4 * i + 2] = __uint_as_float(st.x[m][i].z); xv[m][4 * i + 3] = __uint_as_float(st.x[m][i].w);
+                }
+#pragma unroll
+                for (int e = 0; e < 32; ++e) t += xv[m][e];
+                xs[m][0] = t;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const float q = (float)stream_code<BITS>(st.w[r], e);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) qd[r][m][0] = fmaf(q, xv[m][e], qd[r][m][0]);
+                }
+        }
+    } else if constexpr (use_dot2<DT, BITS>()) {
         // Each word is split into byte-aligned fields (one code per byte); a
         // v_perm places two of those bytes under the magic exponent byte,
         // giving a pair of exact 16-bit codes, and x is paired the same way.
@@ -263,7 +361,7 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint32_t q[PPW];
-                code_pairs<DT, BITS>(word_of(st.w[r], j), q);
+                code_pairs<DT, BITS>(st.w[r][j], q);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     float t = qd[r][m][j / WPP];
@@ -300,7 +398,7 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float q[CPW];
-                unpack_word<BITS>(word_of(st.w[r], j), q);
+                unpack_word<BITS>(st.w[r][j], q);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     float t = qd[r][m][j / WPP];
@@ -356,13 +454,13 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int rr = min(n0 + r, N - 1) - nw;
-        ad.vw[r] = (int)((size_t)rr * row_bytes) + 16 * c;
+        ad.vw[r] = (int)((size_t)rr * row_bytes) + 4 * S::CW * c;
         ad.vsb[r] = (rr * G + (c * S::CPC) / GS) * EB;
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * K + c * S::CPC) * EB;
     // per-round scalar steps
-    constexpr int STEP_W = LP * 16, STEP_SB = LP * S::CPC / GS * EB, STEP_X = LP * S::CPC * EB;
+    constexpr int STEP_W = LP * 4 * S::CW, STEP_SB = LP * S::CPC / GS * EB, STEP_X = LP * S::CPC * EB;
     static_assert((LP * S::CPC) % GS == 0, "a round advances by whole groups");
 
     float acc[R][MT];
@@ -437,7 +535,7 @@ QmvSplit qmv_split_for(int M, int N, int K, int bits) {
     if (qmv_mt_for(M) != 1) return {1, 1};
     static constexpr QmvSplit kCands[] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {4, 1}, {5, 2}, {5, 4}};
     constexpr long kResident = 7 * 1024;
-    const long chunks = (long)K * bits / 128;
+    const long chunks = (long)K / qmv_chunk_codes(bits);
     const bool rows_fill = (long)(N + QMV_ROWS - 1) / QMV_ROWS >= 6000;
     QmvSplit best = {1, 1};
     double best_t = -1.0;
@@ -506,8 +604,12 @@ template <int DT>
 static hipError_t qmv_bits(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                            int M, int N, int K, int bits, int gs, hipStream_t st) {
     switch (bits) {
+        case 1: return qmv_gs<DT, 1>(w, s, b, x, out, M, N, K, gs, st);
         case 2: return qmv_gs<DT, 2>(w, s, b, x, out, M, N, K, gs, st);
+        case 3: return qmv_gs<DT, 3>(w, s, b, x, out, M, N, K, gs, st);
         case 4: return qmv_gs<DT, 4>(w, s, b, x, out, M, N, K, gs, st);
+        case 5: return qmv_gs<DT, 5>(w, s, b, x, out, M, N, K, gs, st);
+        case 6: return qmv_gs<DT, 6>(w, s, b, x, out, M, N, K, gs, st);
         default: return qmv_gs<DT, 8>(w, s, b, x, out, M, N, K, gs, st);
     }
 }

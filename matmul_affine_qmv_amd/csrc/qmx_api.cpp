@@ -27,7 +27,7 @@ size_t elem_bytes(int dt) { return dt == QMX_F32 ? 4 : 2; }
 // Checks shared by every affine route.
 int check_affine_common(int M, int N, int K, int bits, int gs, int dtype) {
     if (dtype != QMX_F32 && dtype != QMX_F16 && dtype != QMX_BF16) return QMX_ERR_DTYPE;
-    if (bits != 2 && bits != 4 && bits != 8) return QMX_ERR_BITS;
+    if (bits < 1 || bits > 8 || bits == 7) return QMX_ERR_BITS;
     if (gs != 32 && gs != 64 && gs != 128) return QMX_ERR_GROUP;
     if (M < 0 || N < 0 || K < 0) return QMX_ERR_SHAPE;
     if (K % gs != 0) return QMX_ERR_GROUP;
@@ -51,7 +51,7 @@ int check_qmv(const uint32_t* w, const void* s, const void* b, const void* x, vo
               int bits, int gs, int dtype) {
     int rc = check_affine_common(M, N, K, bits, gs, dtype);
     if (rc) return rc;
-    if (((long long)K * bits) % 128 != 0) return QMX_ERR_SHAPE;
+    if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
     if (M > 0 && (M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M) > 65535) return QMX_ERR_SHAPE;
     if (M == 0 || N == 0) return QMX_OK;
     return check_affine_ptrs(w, s, b, x, out, K, dtype, 16, 16);
@@ -98,7 +98,7 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     if (num_cus <= 0) num_cus = kDefaultCUs;
     // float32, M < 8 and K that the staged kernel cannot block stay on qmv.
     if (dtype == QMX_F32 || M < 8 || K % QMM_KB != 0) {
-        if (((long long)K * bits) % 128 != 0) return QMX_ERR_SHAPE;
+        if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
         *route = QMX_ROUTE_QMV;
         *splits = 1;
         return QMX_OK;
@@ -129,7 +129,7 @@ const char* qmx_strerror(int status) {
         case QMX_OK: return "success";
         case QMX_ERR_NULL: return "a required pointer is NULL";
         case QMX_ERR_SHAPE: return "unsupported or negative problem size for this route";
-        case QMX_ERR_BITS: return "bits must be 2, 4 or 8";
+        case QMX_ERR_BITS: return "bits must be 1, 2, 3, 4, 5, 6 or 8";
         case QMX_ERR_GROUP: return "group_size must be 32, 64 or 128 and divide K";
         case QMX_ERR_DTYPE: return "unsupported dtype for this route";
         case QMX_ERR_ALIGN: return "a pointer is not aligned as the route requires";

@@ -12,6 +12,13 @@ namespace qmx {
 constexpr int QMV_ROWS = 4;
 int qmv_mt_for(int M);
 
+// A qmv lane reads a row in chunks: 16 bytes for the widths that divide 32
+// (128/bits codes), and for 1, 3, 5 and 6 bits the `bits` words that hold
+// exactly 32 codes (fields may straddle words inside the chunk, never across
+// chunks).
+constexpr int qmv_chunk_words(int bits) { return (bits == 2 || bits == 4 || bits == 8) ? 4 : bits; }
+constexpr int qmv_chunk_codes(int bits) { return 32 * qmv_chunk_words(bits) / bits; }
+
 // qmm_t geometry: 128-column K blocks of 4 MFMA k-steps; 8 waves = 4 along N
 // (2 x 16 columns each) x 2 halves that take alternate k-step pairs.
 constexpr int QMM_WAVES_N = 4;

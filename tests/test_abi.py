@@ -74,8 +74,10 @@ def splitk(splits=2, ws=FAKE, wsb=1 << 30, M=16, N=64, K=4096, bits=4, gs=64, dt
 
 @fake_ptr_test
 def test_qmv_validation():
-    assert qmv(bits=3) == EBITS
-    assert qmv(bits=16) == EBITS
+    for bad in (0, 7, 9, 16):
+        assert qmv(bits=bad) == EBITS
+    for good in (1, 2, 3, 4, 5, 6, 8):   # accepted widths reach the empty-problem exit
+        assert qmv(bits=good, M=0, w=None, x=None, o=None) == OK
     assert qmv(gs=16) == EGROUP
     assert qmv(K=4000) == EGROUP           # not a multiple of 64
     assert qmv(dt=7) == EDTYPE
@@ -96,7 +98,8 @@ def test_qmv_validation():
 def test_qmm_t_validation():
     assert qmm_t(dt=F32) == EDTYPE
     assert qmm_t(K=4032) == ESHAPE          # K % 128 != 0 (but K % 64 == 0)
-    assert qmm_t(bits=5) == EBITS
+    assert qmm_t(bits=7) == EBITS
+    assert qmm_t(bits=5, M=0, w=None) == OK
     assert qmm_t(gs=256) == EGROUP
     assert qmm_t(s=None) == ENULL
     assert qmm_t(x=ODD) == EALIGN
@@ -183,7 +186,10 @@ def test_plan_respects_split_limits():
     with pytest.raises(qmx.QmxError):
         qmx.plan(16, 4096, 96, 2, 32, F32, 256)      # qmv route cannot take 192-bit rows
     with pytest.raises(qmx.QmxError):
-        qmx.plan(1, 4096, 4096, 3, 64, BF16, 256)
+        qmx.plan(1, 4096, 4096, 7, 64, BF16, 256)      # 7-bit codes are not a supported width
+    for bits in (1, 3, 5, 6):                          # the other widths route like 4-bit
+        assert qmx.plan(1, 4096, 4096, bits, 64, BF16, 256) == ("qmv", 1)
+        assert qmx.plan(16, 4096, 4096, bits, 64, BF16, 256) == qmx.plan(16, 4096, 4096, 4, 64, BF16, 256)
 
 
 def test_binding_rejects_cpu_tensors():

@@ -22,6 +22,8 @@ if not torch.cuda.is_available():
 import matmul_affine_qmv_amd as qmx  # noqa: E402
 
 DEV = "cuda:0"
+ALL_BITS = [1, 2, 3, 4, 5, 6, 8]
+ODD_BITS = [1, 3, 5, 6]          # widths whose fields may straddle words (1 bit: 32 codes per word)
 TORCH_DT = {qi.F32: torch.float32, qi.F16: torch.float16, qi.BF16: torch.bfloat16}
 
 
@@ -81,7 +83,7 @@ def check_affine(orc, route, M, N, K, bits, gs, dt, seed, splits=None, cols=None
 
 
 # ---------------------------------------------------------------- qmv
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dt", [qi.F32, qi.F16, qi.BF16])
 def test_qmv_small_all_formats(orc, bits, gs, dt):
@@ -94,6 +96,10 @@ def test_qmv_small_all_formats(orc, bits, gs, dt):
 def test_qmv_small_m(orc, M):
     check_affine(orc, "qmv", M, 45, 1024, 4, 64, qi.BF16, seed=1100 + M)
     check_affine(orc, "qmv", M, 18, 512, 8, 32, qi.F32, seed=1150 + M)
+    for bits in ODD_BITS:
+        check_affine(orc, "qmv", M, 29, 640, bits, 32 if bits != 6 else 128, qi.F16 if bits < 4 else qi.BF16,
+                     seed=1170 + 10 * M + bits)
+        check_affine(orc, "qmv", M, 13, 384, bits, 64, qi.F32, seed=1190 + 10 * M + bits)
 
 
 @pytest.mark.parametrize("N,K,bits,dt", [(67, 256, 4, qi.BF16), (8192, 256, 4, qi.F16), (16384, 256, 4, qi.BF16),
@@ -104,6 +110,15 @@ def test_qmv_work_splits(orc, N, K, bits, dt):
     per row tile x row groups per wave: 1x1, 1x2, 1x4, 2x1, 4x1, 5x2, 5x4);
     ragged N where the shape allows."""
     check_affine(orc, "qmv", 1, N + (3 if N > 4000 else 0), K, bits, 64, dt, seed=1160 + N + K + bits)
+
+
+@pytest.mark.parametrize("bits", ODD_BITS)
+@pytest.mark.parametrize("N,K", [(67, 256), (16384, 256), (67, 1536), (2048, 2560), (6000, 5120), (21, 14336)])
+def test_qmv_odd_width_work_splits(orc, bits, N, K):
+    """The 32-code chunks of the odd widths under every kind of work split the
+    M = 1 rule picks for them, including long rows split over several waves."""
+    check_affine(orc, "qmv", 1, N + (3 if N > 4000 else 0), K, bits, 64, qi.BF16 if bits != 5 else qi.F16,
+                 seed=1400 + N + K + bits)
 
 
 def test_qmv_config1_full(orc):
@@ -124,7 +139,7 @@ def test_qmm_t_small_m_tails(orc, M):
     check_affine(orc, "qmm_t", M, 200, 512, 4, 64, qi.BF16, seed=1200 + M)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
 def test_qmm_t_small_all_formats(orc, bits, gs, dt):
@@ -232,7 +247,8 @@ def test_accumulate_sums_in_order_and_rounds_once(orc):
             assert np.array_equal(out64(out, dt), want)
 
 
-@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.F16), (2, 128, qi.BF16)])
+@pytest.mark.parametrize("bits,gs,dt", [(4, 64, qi.BF16), (2, 32, qi.F16), (8, 128, qi.F16), (2, 128, qi.BF16),
+                                        (3, 64, qi.BF16), (5, 32, qi.F16), (6, 128, qi.BF16), (1, 64, qi.F16)])
 def test_scale_bias_alignment_paths(orc, bits, gs, dt):
     """Scales/biases that start 2 bytes past a 16-byte boundary cannot be staged in
     16-byte chunks; the per-block path must give the same bits as the staged one."""
@@ -257,7 +273,7 @@ def test_scale_bias_alignment_paths(orc, bits, gs, dt):
         assert_close(out64(y_b, dt), orc.affine_case(c), dt, orc, what=f"{route} shifted scales")
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("gs", [32, 64, 128])
 def test_splitk_ragged_partitions(orc, bits, gs):
     """bf16 partitions whose K ranges start and end inside a 16-byte chunk of
@@ -276,7 +292,7 @@ def test_splitk_many_m_tiles(orc):
 
 
 # ---------------------------------------------------------------- affine sweep (bits x gs x dtype x M)
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
 def test_config4_sweep(orc, bits, gs, dt):
