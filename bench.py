@@ -60,6 +60,9 @@ QMM_SHAPES = [(2048, 2048, 22), (4096, 4096, 16), (256, 4096, 16), (10752, 2048,
 WORKLOADS = {
     "qmv_qmm_4bit_gs64_bf16": [affine("qmv", 1, n, k) for n, k in QMV_SHAPES]
     + [affine("qmm", m, n, k) for k, n, m in QMM_SHAPES],
+    # the same calls at the other code widths of the staged loader (1-6 and 8 bits)
+    **{f"qmv_qmm_{b}bit_gs64_bf16": [affine("qmv", 1, n, k, bits=b) for n, k in QMV_SHAPES]
+       + [affine("qmm", m, n, k, bits=b) for k, n, m in QMM_SHAPES] for b in (1, 2, 3, 5, 6, 8)},
     "qmv_4bit_gs64_bf16": [affine("qmv", 1, n, k) for n, k in QMV_SHAPES],
     "qmv_4bit_gs64_f16": [affine("qmv", 1, n, k, F16) for n, k in QMV_SHAPES],
     "qmv_4bit_gs64_f32": [affine("qmv", 1, n, k, F32) for n, k in QMV_SHAPES],
@@ -391,7 +394,8 @@ def main(argv=None):
         cpu = cpu_baseline(calls, sets, args.cpu_seconds)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
+        f"µs/call & effective HBM GB/s (% roofline), workload {args.workload}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

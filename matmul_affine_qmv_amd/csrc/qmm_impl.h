@@ -53,14 +53,20 @@ struct QmmCfg {
     static constexpr int XPT = (BM + 31) / 32;                // x copies per thread per block
     static constexpr int XROWS = 32 * XPT;
     static constexpr int X_BYTES = XROWS * 256;
-    // W: 16*BITS bytes per row per block.  4- and 8-bit rows are copied 16
-    // bytes per lane; 2-bit rows and the widths that do not divide 32 (1, 3,
-    // 5, 6: BITS words of 32 codes, fields straddling words) 4 bytes per lane.
+    // W: 16*BITS bytes per row per block.  1- and 2-bit rows are copied 4
+    // bytes per lane (one and two copies per thread), the others 16 bytes per
+    // lane.  For 3, 5 and 6 bits (fields may straddle words) the 128*BITS
+    // pieces are not a whole number of copies per thread: the spare copies
+    // repeat pieces already covered, writing the same bytes to the same place,
+    // so that every wave still issues the same number of copies.
     static constexpr bool ODD = !(BITS == 2 || BITS == 4 || BITS == 8);
-    static constexpr bool W4B = BITS == 2 || ODD;             // 4-byte W copies
+    static constexpr bool W4B = BITS == 1 || BITS == 2;       // 4-byte W copies
+    static constexpr bool WREP = ODD && !W4B;                 // 16-byte copies with repeats
     static constexpr int W_ROW = 16 * BITS;
     static constexpr int W_BYTES = QMM_BN * W_ROW;
-    static constexpr int WPT = BITS == 4 ? 1 : ODD ? BITS : 2; // W copies per thread per block
+    static constexpr int W_PIECES = W_BYTES / 16;
+    static constexpr int WPT = W4B ? W_BYTES / (4 * QMM_THREADS)
+                             : WREP ? (W_PIECES + QMM_THREADS - 1) / QMM_THREADS : W_BYTES / (16 * QMM_THREADS);
     // Scales then biases.  Staged per block, one 16-bit value per lane
     // (zero-extended to 4 bytes in LDS), unless SBV: then the work-group's whole
     // K range of both is copied once, before the ring, in 16-byte chunks.
@@ -86,7 +92,8 @@ struct QmmCfg {
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
     static_assert(STAGE % 1024 == 0 && X_BYTES % 1024 == 0, "stage alignment");
-    static_assert(WPT * QMM_THREADS * (W4B ? 4 : 16) == W_BYTES, "whole W copies per thread");
+    static_assert(WREP ? W_PIECES % 64 == 0 && WPT * QMM_THREADS >= W_PIECES
+                       : WPT * QMM_THREADS * (W4B ? 4 : 16) == W_BYTES, "W copies per thread");
     static_assert(!SBV || SBV_CHUNKS >= 3, "room for the staged scales and biases");
 };
 
@@ -175,10 +182,14 @@ __device__ __forceinline__ u32x4 expand_stream(uint32_t lo, uint32_t hi, int sh)
             p[j] = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
         }
     } else {
-        const uint64_t v = ((((uint64_t)hi) << 32) | lo) >> (8 * sh);
+        // 40 or 48 bits: the low and high 32-bit halves of the shifted window
+        const uint32_t u0 = __builtin_amdgcn_alignbyte(hi, lo, sh);
+        const uint32_t u1 = __builtin_amdgcn_alignbyte(0u, hi, sh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t t = (uint32_t)(v >> (2 * BITS * j)) & WIN;
+            const int b = 2 * BITS * j;
+            const uint32_t t = (b + 2 * BITS <= 32 ? u0 >> b : b >= 32 ? u1 >> (b - 32)
+                                                             : __builtin_amdgcn_alignbit(u1, u0, b)) & WIN;
             p[j] = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
         }
     }
@@ -279,11 +290,16 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
     for (int j = 0; j < C::WPT; ++j) {
         int R, q;
-        if constexpr (C::ODD) {
-            // word v = 512j + tid of the block, row-major [R][4*BITS] in LDS
+        if constexpr (BITS == 1) {
+            // word v = 512j + tid of the block, row-major [R][4] in LDS
             const int v = QMM_THREADS * j + tid;
-            R = v / (4 * BITS);
-            q = v % (4 * BITS);
+            R = v / 4;
+            q = v % 4;
+        } else if constexpr (C::WREP) {
+            // 16-byte piece v of the block (row v / BITS, piece v % BITS of the row)
+            const int v = (QMM_THREADS * j + tid) % C::W_PIECES;
+            R = v / BITS;
+            q = 4 * (v % BITS);
         } else if constexpr (BITS == 4) {
             R = 16 * wave + (lane >> 2);
             q = 4 * ((lane & 3) ^ ((R >> 2) & 3));
@@ -331,6 +347,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int j = 0; j < C::WPT; ++j) {
             if constexpr (C::W4B)
                 dma<4>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 256);
+            else if constexpr (C::WREP)
+                dma<16>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + ((8 * j + wave) * 1024) % C::W_BYTES);
             else
                 dma<16>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 1024);
         }
