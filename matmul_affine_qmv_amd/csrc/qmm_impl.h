@@ -171,7 +171,7 @@ __device__ __forceinline__ u32x4 expand4(uint32_t w) {
 // bytes.
 template <int DT, int BITS>
 __device__ __forceinline__ u32x4 expand_stream(uint32_t lo, uint32_t hi, int sh) {
-    constexpr uint32_t MB = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    const uint32_t MB = magic_bytes<DT>();
     constexpr uint32_t MASK = (1u << BITS) - 1u, WIN = (1u << (2 * BITS)) - 1u;
     uint32_t p[4];
     if constexpr (8 * BITS <= 32) {

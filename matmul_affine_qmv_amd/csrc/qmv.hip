@@ -245,13 +245,14 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[CW], int e) 
 // The two fields are taken as one 2*BITS-bit window t (code e in its low
 // BITS bits); t | t << (16 - BITS) puts code e + 1 at bit 16, and one mask
 // keeps both codes under the magic bytes.
+// mb holds the magic bytes in a register (see magic_bytes) so that the mask
+// and the magic go into one and-or.
 template <int DT, int BITS, int CW>
-__device__ __forceinline__ uint32_t stream_pair(const uint32_t (&w)[CW], int e) {
-    constexpr uint32_t MB = DT == DT_BF16 ? 0x43004300u : 0x64006400u;
+__device__ __forceinline__ uint32_t stream_pair(const uint32_t (&w)[CW], int e, uint32_t mb) {
     constexpr uint32_t MASK = (1u << BITS) - 1u, WIN = (1u << (2 * BITS)) - 1u;
     const int bit = BITS * e, i = bit >> 5, sh = bit & 31;
     const uint32_t t = (sh + 2 * BITS <= 32 ? w[i] >> sh : __builtin_amdgcn_alignbit(w[i + 1], w[i], sh)) & WIN;
-    uint32_t p = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | MB;
+    uint32_t p = (((t << (16 - BITS)) | t) & (MASK | (MASK << 16))) | mb;
     if constexpr (DT == DT_F16) {
         const h2_t v = __builtin_bit_cast(h2_t, p) - h2_t{(_Float16)1024.f, (_Float16)1024.f};
         p = __builtin_bit_cast(uint32_t, v);
@@ -298,11 +299,12 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
                 for (int k = 0; k < 16; ++k) t = dot2<DT>(xp[m][k], ONES, t);
                 xs[m][0] = t;
             }
+            const uint32_t mb = magic_bytes<DT>();
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    const uint32_t q = stream_pair<DT, BITS>(st.w[r], 2 * k);
+                    const uint32_t q = stream_pair<DT, BITS>(st.w[r], 2 * k, mb);
 #pragma unroll
                     for (int m = 0; m < MT; ++m) qd[r][m][0] = dot2<DT>(q, xp[m][k], qd[r][m][0]);
                 }

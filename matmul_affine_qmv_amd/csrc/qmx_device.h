@@ -67,6 +67,19 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
     return DT == DT_F16 ? f16_bits_to_f32(w >> 16) : __uint_as_float(w & 0xffff0000u);
 }
 
+// ---------------------------------------------------------------- code pairs
+// The magic exponent bytes above a pair of 16-bit codes (0x43 for bf16: the
+// value 128 + q; 0x64 for f16: 1024 + q) as an opaque register value.  With
+// the field mask and the magic both constants, the vector ALU (one scalar
+// operand and no literal in its three-operand forms) needs a separate and and
+// or; with the magic in a register they are one and-or.
+template <int DT>
+__device__ __forceinline__ uint32_t magic_bytes() {
+    uint32_t mb = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    asm volatile("" : "+v"(mb));
+    return mb;
+}
+
 // ---------------------------------------------------------------- wave reductions
 // Sum over all 64 lanes with a fixed butterfly; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
