@@ -211,6 +211,51 @@ const char* qmx_strerror(int status);
 /* QMX_API_VERSION of the built library. */
 int qmx_api_version(void);
 
+/* qmx_qmm_batched -- qmx_qmm over a batch of independent problems of one
+ * shape: 3-D (batched) quantized weights, strided activations and
+ * activations at any element offset (page "mlx PR 4682": the batched
+ * transposed qmm, its test of 3-D quantized weights with strided and
+ * odd-offset activations, and activations that are not suitably aligned
+ * being copied first).
+ *   out[i][m][n] = sum_k x_i[m][k] * (s_i[n,k/gs] * q_i[n,k] + b_i[n,k/gs])
+ * for i < batch, where
+ *   weights i  : w_packed + i*w_batch_stride words (0 shares one matrix;
+ *                a multiple of 4, so every matrix is 16-byte aligned),
+ *   scales/biases i : + i*sb_batch_stride elements (0 shares them),
+ *   x_i rows   : x + i*x_batch_stride + m*x_row_stride elements
+ *                (x_row_stride >= K; any element offset),
+ *   out        : contiguous [batch][M][N] in `dtype`.
+ * Each matrix has the layout of the unbatched calls.  Routes and splits
+ * follow qmx_plan_batched (one launch for the whole batch; split-K partials
+ * are [S][batch][M][N]).  When x, x_batch_stride or x_row_stride is not
+ * 16-byte aligned, x is first copied into the workspace as a contiguous
+ * [batch][M][K] array.  workspace: at least
+ * qmx_qmm_batched_workspace_bytes(...) bytes, 256-byte aligned, may be NULL
+ * when that is 0; contents on entry do not matter; calls sharing one
+ * workspace must be ordered on one stream.
+ * Errors: as qmx_qmm; QMX_ERR_SHAPE for batch outside [0, 65535], a
+ * negative stride or x_row_stride < K; QMX_ERR_ALIGN for a weight stride
+ * that is not a multiple of 4 words.
+ */
+int qmx_qmm_batched(const uint32_t* w_packed, const void* scales, const void* biases,
+                    const void* x, void* out, int batch, int M, int N, int K,
+                    long long w_batch_stride, long long sb_batch_stride,
+                    long long x_batch_stride, long long x_row_stride, int bits,
+                    int group_size, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes qmx_qmm_batched needs (split-K partials as planned on the
+ * current device, plus the copy of x when x or its strides are not 16-byte
+ * aligned; x is only inspected, never dereferenced).  0 on invalid input. */
+size_t qmx_qmm_batched_workspace_bytes(int batch, int M, int N, int K, int bits, int group_size,
+                                       int dtype, const void* x, long long x_batch_stride,
+                                       long long x_row_stride);
+
+/* qmx_plan for a batch: the tiles of all problems share the device, so a
+ * batch needs fewer K partitions.  Pure host function. */
+int qmx_plan_batched(int batch, int M, int N, int K, int bits, int group_size, int dtype,
+                     int num_cus, int* route, int* splits);
+
 #ifdef __cplusplus
 }
 #endif

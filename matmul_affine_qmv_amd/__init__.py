@@ -46,6 +46,11 @@ _EXPORTS = {
     "qmx_qmm_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "qmx_qmm": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
                 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_qmm_batched": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_longlong] * 4
+                        + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_qmm_batched_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 7 + [ctypes.c_void_p]
+                                        + [ctypes.c_longlong] * 2),
+    "qmx_plan_batched": (ctypes.c_int, [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_int)] * 2),
     "qmx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "qmx_api_version": (ctypes.c_int, []),
 }
@@ -241,6 +246,77 @@ def qmm(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64, workspa
     return out
 
 
+def plan_batched(batch, M, N, K, bits=4, group_size=64, dtype=QMX_BF16, num_cus=0):
+    """(route_name, splits) the dispatch policy picks for a batch (pure host call)."""
+    if isinstance(dtype, torch.dtype):
+        dtype = _TORCH_TO_QMX[dtype]
+    route, splits = ctypes.c_int(-1), ctypes.c_int(-1)
+    _check(lib().qmx_plan_batched(batch, M, N, K, bits, group_size, dtype, num_cus, ctypes.byref(route),
+                                  ctypes.byref(splits)), "qmx_plan_batched")
+    return ROUTE_NAMES[route.value], splits.value
+
+
+def qmm_batched(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64, workspace=None):
+    """Batched quantized matmul (qmx_qmm_batched).
+
+    x: [B, M, K] with unit last stride; its batch and row strides and storage
+    offset are passed as they are (rows need not be 16-byte aligned: the
+    library then copies x into the workspace first).  w_packed [B, N, K*bits/32]
+    and scales/biases [B, N, K/group_size], each matrix contiguous, or 2-D to
+    share one matrix across the batch.  out: contiguous [B, M, N]."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [B, M, K] with a unit last stride")
+    B, M, K = x.shape
+    if w_packed.dtype not in _WORD_DTYPES:
+        raise ValueError("w_packed must hold uint32 words (torch.int32 or torch.uint32)")
+    if w_packed.dim() not in (2, 3) or (w_packed.dim() == 3 and w_packed.shape[0] != B):
+        raise ValueError("w_packed must be [N, K*bits/32] or [B, N, K*bits/32]")
+    N, words = w_packed.shape[-2], w_packed.shape[-1]
+    if words * 32 != K * bits:
+        raise ValueError(f"w_packed rows hold {words} words; K={K} at {bits} bits needs {K * bits / 32}")
+    G = K // group_size if group_size else 0
+
+    def batch_stride(t, inner, name):
+        if t.dim() == 2:
+            if tuple(t.shape) != inner:
+                raise ValueError(f"{name} must be {inner} or {(B,) + inner}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            return 0
+        if t.dim() != 3 or tuple(t.shape) != (B,) + inner:
+            raise ValueError(f"{name} must be {inner} or {(B,) + inner}")
+        if t.stride(2) != 1 or t.stride(1) != inner[1]:
+            raise ValueError(f"each matrix of {name} must be contiguous")
+        return t.stride(0) if B > 1 else 0
+
+    wbs = batch_stride(w_packed, (N, K * bits // 32), "w_packed")
+    sbs = batch_stride(scales, (N, G), "scales")
+    if batch_stride(biases, (N, G), "biases") != sbs:
+        raise ValueError("scales and biases must share their batch stride")
+    for name, t in (("scales", scales), ("biases", biases)):
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype {x.dtype}")
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != (B, M, N) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [B, M, N] = {(B, M, N)} of dtype {x.dtype}")
+    for t in (w_packed, scales, biases, x, out):
+        if not t.is_cuda or t.device != x.device:
+            raise ValueError("all tensors must be on x's HIP device")
+    xs = x.stride(0) if B > 1 else 0
+    xr = x.stride(1) if M > 1 else K
+    dt = _dtype_code(x)
+    need = lib().qmx_qmm_batched_workspace_bytes(B, M, N, K, bits, group_size, dt, _ptr(x), xs, xr)
+    if need and workspace is None:
+        workspace = _workspace(x, need, None)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().qmx_qmm_batched(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), B, M, N, K,
+                                 wbs, sbs, xs, xr, bits, group_size, dt, ws_ptr, ws_bytes, _stream(x)),
+           "qmx_qmm_batched")
+    return out
+
+
 def _block_args(w_blocks, x, out, words_per_block, weights_per_block):
     if x.dim() != 1 or x.dtype != torch.float32:
         raise ValueError("x must be a float32 vector [K]")
@@ -297,7 +373,8 @@ def tensor_bits(t: torch.Tensor):
     return t.numpy()
 
 
-__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "plan", "matvec_q8_0", "matvec_q4_k",
+__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "qmm_batched", "plan", "plan_batched", "matvec_q8_0",
+           "matvec_q4_k",
            "splitk_workspace_bytes", "qmm_workspace_bytes", "strerror", "api_version", "lib",
            "QmxError", "words_tensor", "storage_tensor", "tensor_bits",
            "QMX_F32", "QMX_F16", "QMX_BF16"]

@@ -23,16 +23,16 @@ int qmm_mt_for(int M) {
 int qmm_mtiles_for(int M) { return M <= 192 ? (M + 63) / 64 : (M + 127) / 128; }
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                        float* ws, int M, int N, int K, int bits, int gs, int dt, int splits,
-                        hipStream_t st) {
+                        float* ws, int batch, QmxStrides sd, int M, int N, int K, int bits, int gs,
+                        int dt, int splits, hipStream_t st) {
     switch (bits) {
-        case 1: return qmm_launch_b1(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        case 2: return qmm_launch_b2(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        case 3: return qmm_launch_b3(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        case 4: return qmm_launch_b4(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        case 5: return qmm_launch_b5(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        case 6: return qmm_launch_b6(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
-        default: return qmm_launch_b8(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+        case 1: return qmm_launch_b1(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        case 2: return qmm_launch_b2(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        case 3: return qmm_launch_b3(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        case 4: return qmm_launch_b4(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        case 5: return qmm_launch_b5(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        case 6: return qmm_launch_b6(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
+        default: return qmm_launch_b8(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
     }
 }
 

@@ -5,8 +5,9 @@
 namespace qmx {
 
 hipError_t qmm_launch_b8(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         float* ws, int M, int N, int K, int gs, int dt, int splits, hipStream_t st) {
-    return qmm_launch_bits<8>(w, s, b, x, out, ws, M, N, K, gs, dt, splits, st);
+                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int gs, int dt, int splits,
+                         hipStream_t st) {
+    return qmm_launch_bits<8>(w, s, b, x, out, ws, batch, sd, M, N, K, gs, dt, splits, st);
 }
 
 }  // namespace qmx

@@ -245,9 +245,17 @@ __device__ __forceinline__ void stage_barrier() {
 template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
-    const void* __restrict__ x, void* __restrict__ out, float* __restrict__ ws,
+    const void* __restrict__ x, void* __restrict__ out, float* __restrict__ ws, QmxStrides sd,
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
     using C = QmmCfg<DT, BITS, GS, MT, SBV>;
+    // problem blockIdx.y of the batch (16-bit x, scales, biases and out)
+    const long long bz = blockIdx.y;
+    w += bz * sd.w;
+    scales = static_cast<const uint16_t*>(scales) + bz * sd.sb;
+    biases = static_cast<const uint16_t*>(biases) + bz * sd.sb;
+    x = static_cast<const uint16_t*>(x) + bz * sd.x;
+    if constexpr (!SPLIT) out = static_cast<uint16_t*>(out) + bz * M * (long long)N;
+    const long long XR = sd.x_row;
     constexpr int NB = QMM_NB;
     constexpr int NS = C::NS;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * C::STAGE + C::SBV_BYTES];
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     for (int i = 0; i < C::XPT; ++i) {
         const int r = 4 * (8 * i + wave) + (lane >> 4);
         const int c = (lane & 15) ^ (r & 15);
-        xsrc[i] = static_cast<const uint16_t*>(x) + (size_t)min(m0 + r, M - 1) * K + 8 * c;
+        xsrc[i] = static_cast<const uint16_t*>(x) + min(m0 + r, M - 1) * XR + 8 * c;
     }
     // W: tile rows R in 16-byte chunks (4-byte words for 2-bit codes); the chunk a
     // slot holds is its index XOR a few bits of R, so B-operand reads spread over banks.
@@ -543,7 +551,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int v = 0; v < 4; ++v) {
             const int m = m0 + mf * 16 + 4 * lgrp + v;
             if (m < M) {
-                const size_t row = SPLIT ? ((size_t)split * M + m) * N : (size_t)m * N;
+                const size_t row = SPLIT ? (((size_t)split * gridDim.y + bz) * M + m) * N : (size_t)m * N;
 #pragma unroll
                 for (int nf = 0; nf < NB; ++nf) {
                     const int n = nl + nf * 16;
@@ -560,80 +568,86 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 
 template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
 void qmm_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out, float* ws,
-            int M, int N, int K, int splits, int ntiles, int mtiles, int total, int per_xcd, hipStream_t st) {
+            QmxStrides sd, int M, int N, int K, int splits, int ntiles, int mtiles, int total, int per_xcd,
+            hipStream_t st) {
     hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV>), grid, dim3(QMM_THREADS), 0, st, w, s, b, x,
-                       out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd);
+                       out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd);
 }
 
 template <int DT, int BITS, int GS, int MT>
 hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         float* ws, int M, int N, int K, int splits, hipStream_t st) {
+                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
     const int ntiles = (N + QMM_BN - 1) / QMM_BN;
     const int mtiles = qmm_mtiles_for(M);
     const int total = ntiles * mtiles * splits;
     const int per_xcd = (total + 7) / 8;
-    const dim3 grid(8 * per_xcd);
+    const dim3 grid(8 * per_xcd, batch);
     // Staged scales/biases need 16-byte aligned arrays, rows of whole 16-byte chunks
     // (K/GS a multiple of 8) and a K range whose chunks (plus one for alignment and
     // one for an odd count) fit the LDS left over.
     const int G = K / GS, nkb = K / QMM_KB;
     const int nk_max = (nkb + splits - 1) / splits;
-    const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
+                         (sd.sb * 2) % 16 == 0;
     const bool sbv = aligned && K > 0 && G % 8 == 0 &&
                      (nk_max * (QMM_KB / GS) + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT>();
+#define QMM_GO(SPLIT_, SBV_) \
+    qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
     if (splits > 1) {
-        if (sbv) qmm_go<DT, BITS, GS, MT, true, true>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
-        else qmm_go<DT, BITS, GS, MT, true, false>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+        if (sbv) QMM_GO(true, true);
+        else QMM_GO(true, false);
     } else {
-        if (sbv) qmm_go<DT, BITS, GS, MT, false, true>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
-        else qmm_go<DT, BITS, GS, MT, false, false>(grid, w, s, b, x, out, ws, M, N, K, splits, ntiles, mtiles, total, per_xcd, st);
+        if (sbv) QMM_GO(false, true);
+        else QMM_GO(false, false);
     }
+#undef QMM_GO
     return hipGetLastError();
 }
 
 template <int DT, int BITS, int GS>
 hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         float* ws, int M, int N, int K, int splits, hipStream_t st) {
+                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
     switch (qmm_mt_for(M)) {
-        case 1: return qmm_launch_mt<DT, BITS, GS, 1>(w, s, b, x, out, ws, M, N, K, splits, st);
-        case 2: return qmm_launch_mt<DT, BITS, GS, 2>(w, s, b, x, out, ws, M, N, K, splits, st);
-        case 3: return qmm_launch_mt<DT, BITS, GS, 3>(w, s, b, x, out, ws, M, N, K, splits, st);
-        case 4: return qmm_launch_mt<DT, BITS, GS, 4>(w, s, b, x, out, ws, M, N, K, splits, st);
-        case 6: return qmm_launch_mt<DT, BITS, GS, 6>(w, s, b, x, out, ws, M, N, K, splits, st);
-        default: return qmm_launch_mt<DT, BITS, GS, 8>(w, s, b, x, out, ws, M, N, K, splits, st);
+        case 1: return qmm_launch_mt<DT, BITS, GS, 1>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        case 2: return qmm_launch_mt<DT, BITS, GS, 2>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        case 3: return qmm_launch_mt<DT, BITS, GS, 3>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        case 4: return qmm_launch_mt<DT, BITS, GS, 4>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        case 6: return qmm_launch_mt<DT, BITS, GS, 6>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        default: return qmm_launch_mt<DT, BITS, GS, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
     }
 }
 
 template <int BITS>
 hipError_t qmm_launch_bits(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                           float* ws, int M, int N, int K, int gs, int dt, int splits, hipStream_t st) {
+                           float* ws, int batch, QmxStrides sd, int M, int N, int K, int gs, int dt, int splits,
+                           hipStream_t st) {
     if (dt == DT_F16) {
         switch (gs) {
-            case 32: return qmm_launch_gs<DT_F16, BITS, 32>(w, s, b, x, out, ws, M, N, K, splits, st);
-            case 64: return qmm_launch_gs<DT_F16, BITS, 64>(w, s, b, x, out, ws, M, N, K, splits, st);
-            default: return qmm_launch_gs<DT_F16, BITS, 128>(w, s, b, x, out, ws, M, N, K, splits, st);
+            case 32: return qmm_launch_gs<DT_F16, BITS, 32>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+            case 64: return qmm_launch_gs<DT_F16, BITS, 64>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+            default: return qmm_launch_gs<DT_F16, BITS, 128>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
         }
     }
     switch (gs) {
-        case 32: return qmm_launch_gs<DT_BF16, BITS, 32>(w, s, b, x, out, ws, M, N, K, splits, st);
-        case 64: return qmm_launch_gs<DT_BF16, BITS, 64>(w, s, b, x, out, ws, M, N, K, splits, st);
-        default: return qmm_launch_gs<DT_BF16, BITS, 128>(w, s, b, x, out, ws, M, N, K, splits, st);
+        case 32: return qmm_launch_gs<DT_BF16, BITS, 32>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        case 64: return qmm_launch_gs<DT_BF16, BITS, 64>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+        default: return qmm_launch_gs<DT_BF16, BITS, 128>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
     }
 }
 
-hipError_t qmm_launch_b1(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b2(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b3(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b4(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b5(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b6(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
-hipError_t qmm_launch_b8(const uint32_t*, const void*, const void*, const void*, void*, float*, int, int,
-                         int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b1(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b2(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b3(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b4(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b5(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b6(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
+hipError_t qmm_launch_b8(const uint32_t*, const void*, const void*, const void*, void*, float*, int, QmxStrides,
+                         int, int, int, int, int, int, hipStream_t);
 
 }  // namespace qmx

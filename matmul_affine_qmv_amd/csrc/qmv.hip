@@ -429,10 +429,22 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
                                                           const void* __restrict__ scales,
                                                           const void* __restrict__ biases,
                                                           const void* __restrict__ x,
-                                                          void* __restrict__ out, int M, int N, int K) {
+                                                          void* __restrict__ out, QmxStrides sd, int M, int N,
+                                                          int K) {
     constexpr int R = QMV_ROWS;
     constexpr int LP = 64 / RG;   // lanes per row group
     using S = QmvStage<DT, BITS, GS, MT>;
+    // problem blockIdx.z of the batch
+    {
+        constexpr int E = DT == DT_F32 ? 4 : 2;
+        const long long bz = blockIdx.z;
+        w += bz * sd.w;
+        scales = static_cast<const unsigned char*>(scales) + bz * sd.sb * E;
+        biases = static_cast<const unsigned char*>(biases) + bz * sd.sb * E;
+        x = static_cast<const unsigned char*>(x) + bz * sd.x * E;
+        out = static_cast<unsigned char*>(out) + bz * M * (long long)N * E;
+    }
+    const int XR = (int)sd.x_row;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lp = lane / LP, ll = lane % LP;
     const int nw = blockIdx.x * RG * R;          // first row of the work-group
@@ -452,7 +464,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     ad.w = buffer_over(reinterpret_cast<const unsigned char*>(w) + (size_t)nw * row_bytes, (size_t)(N - nw) * row_bytes);
     ad.s = buffer_over(static_cast<const unsigned char*>(scales) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
     ad.b = buffer_over(static_cast<const unsigned char*>(biases) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
-    ad.x = buffer_over(static_cast<const unsigned char*>(x) + (size_t)m0 * K * EB, (size_t)(M - m0) * K * EB);
+    ad.x = buffer_over(static_cast<const unsigned char*>(x) + (size_t)m0 * XR * EB,
+                       ((size_t)(M - m0 - 1) * XR + K) * EB);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int rr = min(n0 + r, N - 1) - nw;
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
         ad.vsb[r] = (rr * G + (c * S::CPC) / GS) * EB;
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * K + c * S::CPC) * EB;
+    for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * XR + c * S::CPC) * EB;
     // per-round scalar steps
     constexpr int STEP_W = LP * 4 * S::CW, STEP_SB = LP * S::CPC / GS * EB, STEP_X = LP * S::CPC * EB;
     static_assert((LP * S::CPC) % GS == 0, "a round advances by whole groups");
@@ -518,9 +531,6 @@ int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
 // the same rows, and RG row groups of QMV_ROWS rows share one wave (64 / RG
 // lanes each).  Each wave walks its chunks in rounds of 64 / RG (one per lane),
 // every round a dependent memory round trip.
-struct QmvSplit {
-    int ks, rg;
-};
 
 // Measured on the chip (sweeps of every split on the four 4-bit shapes with K =
 // 5120 or 14336): a wave-round (one round of one wave, whatever its lane use)
@@ -533,7 +543,7 @@ struct QmvSplit {
 // with the lowest max(wave-rounds per SIMD * (1 + 0.1 (RG - 1)) us, rounds *
 // 1.6 us) + 0.5 us * (generations - 1) wins; ties go to fewer rounds, then to
 // fewer waves per row tile.
-QmvSplit qmv_split_for(int M, int N, int K, int bits) {
+QmvSplit qmv_split_for(int M, long long N, int K, int bits) {
     if (qmv_mt_for(M) != 1) return {1, 1};
     static constexpr QmvSplit kCands[] = {{1, 1}, {1, 2}, {1, 4}, {2, 1}, {4, 1}, {5, 2}, {5, 4}};
     constexpr long kResident = 7 * 1024;
@@ -562,67 +572,101 @@ QmvSplit qmv_split_for(int M, int N, int K, int bits) {
 }
 
 template <int DT, int BITS, int GS, int MT, int KS, int RG>
-static void qmv_go(int M, int N, int K, const uint32_t* w, const void* s, const void* b, const void* x,
-                   void* out, hipStream_t st) {
-    const dim3 grid((N + QMV_ROWS * RG - 1) / (QMV_ROWS * RG), (M + MT - 1) / MT);
-    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS, RG>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, M,
-                       N, K);
+static void qmv_go(int batch, QmxStrides sd, int M, int N, int K, const uint32_t* w, const void* s, const void* b,
+                   const void* x, void* out, hipStream_t st) {
+    const dim3 grid((N + QMV_ROWS * RG - 1) / (QMV_ROWS * RG), (M + MT - 1) / MT, batch);
+    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS, RG>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, sd,
+                       M, N, K);
 }
 
 template <int DT, int BITS, int GS>
-static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         int M, int N, int K, hipStream_t st) {
+static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
+                         QmxStrides sd, int M, int N, int K, hipStream_t st) {
     const int mt = qmv_mt_for(M);
+#define QMV_GO(MT_, KS_, RG_) qmv_go<DT, BITS, GS, MT_, KS_, RG_>(batch, sd, M, N, K, w, s, b, x, out, st)
     if (mt == 1) {
-        const QmvSplit sp = qmv_split_for(M, N, K, BITS);
+        const QmvSplit sp = qmv_split_for(M, (long long)N * batch, K, BITS);
         switch (sp.ks * 8 + sp.rg) {
-            case 1 * 8 + 2: qmv_go<DT, BITS, GS, 1, 1, 2>(M, N, K, w, s, b, x, out, st); break;
-            case 1 * 8 + 4: qmv_go<DT, BITS, GS, 1, 1, 4>(M, N, K, w, s, b, x, out, st); break;
-            case 2 * 8 + 1: qmv_go<DT, BITS, GS, 1, 2, 1>(M, N, K, w, s, b, x, out, st); break;
-            case 4 * 8 + 1: qmv_go<DT, BITS, GS, 1, 4, 1>(M, N, K, w, s, b, x, out, st); break;
-            case 5 * 8 + 2: qmv_go<DT, BITS, GS, 1, 5, 2>(M, N, K, w, s, b, x, out, st); break;
-            case 5 * 8 + 4: qmv_go<DT, BITS, GS, 1, 5, 4>(M, N, K, w, s, b, x, out, st); break;
-            default: qmv_go<DT, BITS, GS, 1, 1, 1>(M, N, K, w, s, b, x, out, st); break;
+            case 1 * 8 + 2: QMV_GO(1, 1, 2); break;
+            case 1 * 8 + 4: QMV_GO(1, 1, 4); break;
+            case 2 * 8 + 1: QMV_GO(1, 2, 1); break;
+            case 4 * 8 + 1: QMV_GO(1, 4, 1); break;
+            case 5 * 8 + 2: QMV_GO(1, 5, 2); break;
+            case 5 * 8 + 4: QMV_GO(1, 5, 4); break;
+            default: QMV_GO(1, 1, 1); break;
         }
     } else if (mt == 2) {
-        qmv_go<DT, BITS, GS, 2, 1, 1>(M, N, K, w, s, b, x, out, st);
+        QMV_GO(2, 1, 1);
     } else {
-        qmv_go<DT, BITS, GS, 4, 1, 1>(M, N, K, w, s, b, x, out, st);
+        QMV_GO(4, 1, 1);
     }
+#undef QMV_GO
     return hipGetLastError();
 }
 
 template <int DT, int BITS>
-static hipError_t qmv_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         int M, int N, int K, int gs, hipStream_t st) {
+static hipError_t qmv_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
+                         QmxStrides sd, int M, int N, int K, int gs, hipStream_t st) {
     switch (gs) {
-        case 32: return qmv_mt<DT, BITS, 32>(w, s, b, x, out, M, N, K, st);
-        case 64: return qmv_mt<DT, BITS, 64>(w, s, b, x, out, M, N, K, st);
-        default: return qmv_mt<DT, BITS, 128>(w, s, b, x, out, M, N, K, st);
+        case 32: return qmv_mt<DT, BITS, 32>(w, s, b, x, out, batch, sd, M, N, K, st);
+        case 64: return qmv_mt<DT, BITS, 64>(w, s, b, x, out, batch, sd, M, N, K, st);
+        default: return qmv_mt<DT, BITS, 128>(w, s, b, x, out, batch, sd, M, N, K, st);
     }
 }
 
 template <int DT>
-static hipError_t qmv_bits(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                           int M, int N, int K, int bits, int gs, hipStream_t st) {
+static hipError_t qmv_bits(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
+                           QmxStrides sd, int M, int N, int K, int bits, int gs, hipStream_t st) {
     switch (bits) {
-        case 1: return qmv_gs<DT, 1>(w, s, b, x, out, M, N, K, gs, st);
-        case 2: return qmv_gs<DT, 2>(w, s, b, x, out, M, N, K, gs, st);
-        case 3: return qmv_gs<DT, 3>(w, s, b, x, out, M, N, K, gs, st);
-        case 4: return qmv_gs<DT, 4>(w, s, b, x, out, M, N, K, gs, st);
-        case 5: return qmv_gs<DT, 5>(w, s, b, x, out, M, N, K, gs, st);
-        case 6: return qmv_gs<DT, 6>(w, s, b, x, out, M, N, K, gs, st);
-        default: return qmv_gs<DT, 8>(w, s, b, x, out, M, N, K, gs, st);
+        case 1: return qmv_gs<DT, 1>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 2: return qmv_gs<DT, 2>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 3: return qmv_gs<DT, 3>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 4: return qmv_gs<DT, 4>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 5: return qmv_gs<DT, 5>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 6: return qmv_gs<DT, 6>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        default: return qmv_gs<DT, 8>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
     }
 }
 
 hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                      int M, int N, int K, int bits, int gs, int dt, hipStream_t st) {
+                      int batch, QmxStrides sd, int M, int N, int K, int bits, int gs, int dt,
+                      hipStream_t st) {
     switch (dt) {
-        case DT_F32: return qmv_bits<DT_F32>(w, s, b, x, out, M, N, K, bits, gs, st);
-        case DT_F16: return qmv_bits<DT_F16>(w, s, b, x, out, M, N, K, bits, gs, st);
-        default: return qmv_bits<DT_BF16>(w, s, b, x, out, M, N, K, bits, gs, st);
+        case DT_F32: return qmv_bits<DT_F32>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
+        case DT_F16: return qmv_bits<DT_F16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
+        default: return qmv_bits<DT_BF16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
     }
+}
+
+// Strided rows -> contiguous rows (for activations whose rows are not 16-byte
+// aligned): work-groups stride over the batch*M rows, threads over a row's
+// elements, one element each (the source alignment rules out wider loads).
+template <int E>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const unsigned char* __restrict__ x,
+                                                        unsigned char* __restrict__ dst, long long xs,
+                                                        long long xr, int M, int K, long long rows) {
+    for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
+        const long long bz = row / M, m = row - bz * M;
+        const unsigned char* src = x + (bz * xs + m * xr) * E;
+        unsigned char* d = dst + row * K * E;
+        for (int i = threadIdx.x; i < K; i += 256) {
+            if constexpr (E == 4) reinterpret_cast<uint32_t*>(d)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+            else reinterpret_cast<uint16_t*>(d)[i] = reinterpret_cast<const uint16_t*>(src)[i];
+        }
+    }
+}
+
+hipError_t launch_copy_rows(const void* x, void* dst, int batch, long long xs, long long xr, int M, int K,
+                            int elem, hipStream_t st) {
+    const long long rows = (long long)batch * M;
+    const dim3 grid((unsigned)(rows < 8192 ? rows : 8192));
+    if (elem == 4)
+        hipLaunchKernelGGL(copy_rows_kernel<4>, grid, dim3(256), 0, st, static_cast<const unsigned char*>(x),
+                           static_cast<unsigned char*>(dst), xs, xr, M, K, rows);
+    else
+        hipLaunchKernelGGL(copy_rows_kernel<2>, grid, dim3(256), 0, st, static_cast<const unsigned char*>(x),
+                           static_cast<unsigned char*>(dst), xs, xr, M, K, rows);
+    return hipGetLastError();
 }
 
 }  // namespace qmx

@@ -92,7 +92,8 @@ int device_cus() {
     return cus;
 }
 
-int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int* route, int* splits) {
+int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int* route, int* splits,
+              int batch = 1) {
     int rc = check_affine_common(M, N, K, bits, gs, dtype);
     if (rc) return rc;
     if (num_cus <= 0) num_cus = kDefaultCUs;
@@ -103,7 +104,7 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
         *splits = 1;
         return QMX_OK;
     }
-    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
+    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M) * batch;
     *route = QMX_ROUTE_QMM_T;
     *splits = 1;
     if (K < 4 * QMM_KB || tiles >= num_cus || tiles == 0) return QMX_OK;
@@ -145,16 +146,16 @@ int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases, co
             int M, int N, int K, int bits, int group_size, int dtype, void* stream) {
     const int rc = check_qmv(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype);
     if (rc || M == 0 || N == 0) return rc;
-    return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype,
-                                         static_cast<hipStream_t>(stream)));
+    return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, 1, qmx::unbatched(K), M, N, K, bits,
+                                         group_size, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int qmx_qmm_t(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
               int M, int N, int K, int bits, int group_size, int dtype, void* stream) {
     const int rc = check_qmm(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, 1);
     if (rc || M == 0 || N == 0) return rc;
-    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, M, N, K, bits,
-                                           group_size, dtype, 1, static_cast<hipStream_t>(stream)));
+    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, 1, qmx::unbatched(K), M, N,
+                                           K, bits, group_size, dtype, 1, static_cast<hipStream_t>(stream)));
 }
 
 size_t qmx_splitk_workspace_bytes(int M, int N, int splits) {
@@ -174,8 +175,9 @@ int qmx_qmm_t_partials(const uint32_t* w_packed, const void* scales, const void*
     if (M == 0 || N == 0) return QMX_OK;
     if (!workspace || !is_aligned(workspace, 16) || workspace_bytes < qmx_splitk_workspace_bytes(M, N, splits))
         return QMX_ERR_WORKSPACE;
-    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, nullptr, static_cast<float*>(workspace), M,
-                                           N, K, bits, group_size, dtype, splits, static_cast<hipStream_t>(stream)));
+    return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, nullptr, static_cast<float*>(workspace), 1,
+                                           qmx::unbatched(K), M, N, K, bits, group_size, dtype, splits,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int qmx_splitk_accumulate(const void* workspace, void* out, int M, int N, int splits, int dtype, void* stream) {
@@ -203,8 +205,8 @@ int qmx_qmm_t_splitk(const uint32_t* w_packed, const void* scales, const void* b
         return QMX_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     float* ws = static_cast<float*>(workspace);
-    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, M, N, K, bits, group_size,
-                                         dtype, splits, st));
+    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, 1, qmx::unbatched(K), M, N, K, bits,
+                                         group_size, dtype, splits, st));
     if (rc) return rc;
     return launch_status(qmx::launch_splitk_accum(ws, out, splits, (size_t)M * N, dtype, st));
 }
@@ -257,6 +259,101 @@ int qmx_qmm(const uint32_t* w_packed, const void* scales, const void* biases, co
         return qmx_qmm_t(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, stream);
     return qmx_qmm_t_splitk(w_packed, scales, biases, x, out, M, N, K, bits, group_size, dtype, splits,
                             workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- batched
+// Workspace layout of a batched call: the split-K partials (rounded up to 256
+// bytes), then, when x must be copied, the contiguous copy of x.
+static size_t batched_partials_bytes(int batch, int M, int N, int route, int splits) {
+    if (route != QMX_ROUTE_QMM_T_SPLITK) return 0;
+    return ((size_t)splits * batch * M * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+static bool x_needs_copy(const void* x, long long xs, long long xr, int dtype) {
+    const long long e = (long long)elem_bytes(dtype);
+    return !is_aligned(x, 16) || (xs * e) % 16 != 0 || (xr * e) % 16 != 0;
+}
+
+static int check_batched(int batch, int M, int N, int K, long long ws_, long long sbs, long long xs, long long xr,
+                         int bits, int gs, int dtype) {
+    int rc = check_affine_common(M, N, K, bits, gs, dtype);
+    if (rc) return rc;
+    if (batch < 0 || batch > 65535 || ws_ < 0 || sbs < 0 || xs < 0 || xr < K) return QMX_ERR_SHAPE;
+    // per-problem lane offsets of the vector-ALU route stay in 32 bits
+    if (xr > ((1LL << 31) - 1) / 8 / (long long)elem_bytes(dtype)) return QMX_ERR_SHAPE;
+    if (ws_ % 4 != 0) return QMX_ERR_ALIGN;   // every weight matrix starts 16-byte aligned
+    return QMX_OK;
+}
+
+int qmx_plan_batched(int batch, int M, int N, int K, int bits, int group_size, int dtype, int num_cus, int* route,
+                     int* splits) {
+    if (!route || !splits) return QMX_ERR_NULL;
+    if (batch < 0 || batch > 65535) return QMX_ERR_SHAPE;
+    return plan_impl(M, N, K, bits, group_size, dtype, num_cus, route, splits, batch > 0 ? batch : 1);
+}
+
+size_t qmx_qmm_batched_workspace_bytes(int batch, int M, int N, int K, int bits, int group_size, int dtype,
+                                       const void* x, long long x_batch_stride, long long x_row_stride) {
+    int route = 0, splits = 1;
+    if (check_batched(batch, M, N, K, 0, 0, x_batch_stride, x_row_stride, bits, group_size, dtype) != QMX_OK)
+        return 0;
+    if (batch == 0 || M == 0 || N == 0) return 0;
+    if (plan_impl(M, N, K, bits, group_size, dtype, device_cus(), &route, &splits, batch) != QMX_OK) return 0;
+    size_t bytes = batched_partials_bytes(batch, M, N, route, splits);
+    if (K > 0 && x_needs_copy(x, x_batch_stride, x_row_stride, dtype))
+        bytes += (size_t)batch * M * K * elem_bytes(dtype);
+    return bytes;
+}
+
+int qmx_qmm_batched(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
+                    int batch, int M, int N, int K, long long w_batch_stride, long long sb_batch_stride,
+                    long long x_batch_stride, long long x_row_stride, int bits, int group_size, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_batched(batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, bits,
+                           group_size, dtype);
+    if (rc) return rc;
+    if (batch == 0 || M == 0 || N == 0) return QMX_OK;
+    const int cus = device_cus();
+    if (cus <= 0) return QMX_ERR_DEVICE;
+    int route = 0, splits = 1;
+    rc = plan_impl(M, N, K, bits, group_size, dtype, cus, &route, &splits, batch);
+    if (rc) return rc;
+    if (route == QMX_ROUTE_QMV) {
+        if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
+        if ((long long)((M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M)) > 65535) return QMX_ERR_SHAPE;
+    } else if (route == QMX_ROUTE_QMM_T || route == QMX_ROUTE_QMM_T_SPLITK) {
+        const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
+        if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
+    }
+    const bool copy_x = K > 0 && x_needs_copy(x, x_batch_stride, x_row_stride, dtype);
+    // pointer checks: x may be at any element offset when it is copied first
+    rc = check_affine_ptrs(w_packed, scales, biases, x, out, K, dtype, 16, copy_x ? elem_bytes(dtype) : 16);
+    if (rc) return rc;
+    const size_t part_bytes = batched_partials_bytes(batch, M, N, route, splits);
+    const size_t need = part_bytes + (copy_x ? (size_t)batch * M * K * elem_bytes(dtype) : 0);
+    if (need > 0 && (!workspace || !is_aligned(workspace, 256) || workspace_bytes < need)) return QMX_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    qmx::QmxStrides sd{w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride};
+    if (copy_x) {
+        void* xc = static_cast<unsigned char*>(workspace) + part_bytes;
+        rc = launch_status(qmx::launch_copy_rows(x, xc, batch, x_batch_stride, x_row_stride, M, K,
+                                                 (int)elem_bytes(dtype), st));
+        if (rc) return rc;
+        x = xc;
+        sd.x = (long long)M * K;
+        sd.x_row = K;
+    }
+    if (route == QMX_ROUTE_QMV)
+        return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, batch, sd, M, N, K, bits, group_size,
+                                             dtype, st));
+    if (route == QMX_ROUTE_QMM_T)
+        return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, batch, sd, M, N, K, bits,
+                                               group_size, dtype, 1, st));
+    float* ws = static_cast<float*>(workspace);
+    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, batch, sd, M, N, K, bits, group_size,
+                                         dtype, splits, st));
+    if (rc) return rc;
+    return launch_status(qmx::launch_splitk_accum(ws, out, splits, (size_t)batch * M * N, dtype, st));
 }
 
 }  // extern "C"

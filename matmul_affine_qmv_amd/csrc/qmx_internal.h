@@ -30,14 +30,36 @@ constexpr int QMM_THREADS = 2 * QMM_WAVES_N * 64;
 int qmm_mt_for(int M);
 int qmm_mtiles_for(int M);
 
+// A batch of independent problems of one shape: problem i reads weights
+// `i * w` words, scales and biases `i * sb` elements and x `i * x` elements
+// after the first (a stride of 0 shares that operand), x rows are `x_row`
+// elements apart (>= K), and it writes output matrix i of a contiguous
+// [batch][M][N] (split-K partials: [S][batch][M][N]).
+struct QmxStrides {
+    long long w, sb, x, x_row;
+};
+inline QmxStrides unbatched(int K) { return QmxStrides{0, 0, 0, K}; }
+
+// M = 1 work split chosen for `rows` rows of W in all (N times the batch).
+struct QmvSplit {
+    int ks, rg;
+};
+QmvSplit qmv_split_for(int M, long long rows, int K, int bits);
+
 hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                      int M, int N, int K, int bits, int gs, int dt, hipStream_t st);
+                      int batch, QmxStrides sd, int M, int N, int K, int bits, int gs, int dt,
+                      hipStream_t st);
 
 // splits == 1: writes `out` in dtype dt.  splits > 1: writes float32
-// partials ws[p][M][N] (the accumulate kernel is launched separately).
+// partials ws[p][batch][M][N] (the accumulate kernel is launched separately).
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                        float* ws, int M, int N, int K, int bits, int gs, int dt, int splits,
-                        hipStream_t st);
+                        float* ws, int batch, QmxStrides sd, int M, int N, int K, int bits, int gs,
+                        int dt, int splits, hipStream_t st);
+
+// Copies a batch of strided matrices [batch][M][K] (elements of `elem` bytes,
+// matrix stride `xs`, row stride `xr`) into a contiguous array.
+hipError_t launch_copy_rows(const void* x, void* dst, int batch, long long xs, long long xr, int M, int K,
+                            int elem, hipStream_t st);
 
 hipError_t launch_splitk_accum(const float* ws, void* out, int splits, size_t MN, int dt,
                                hipStream_t st);

@@ -199,3 +199,38 @@ def test_binding_rejects_cpu_tensors():
     s = torch.zeros(8, 1, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qmx.qmv(w, s, s, x, bits=4, group_size=64)
+
+
+@fake_ptr_test
+def test_batched_validation():
+    L = qmx.lib()
+
+    def bat(B=2, M=4, N=64, K=512, ws=128, sbs=64, xs=2048, xr=512, bits=4, gs=64, dt=BF16, w=FAKE, x=FAKE,
+            o=FAKE, work=None, wb=0):
+        return L.qmx_qmm_batched(w, FAKE, FAKE, x, o, B, M, N, K, ws, sbs, xs, xr, bits, gs, dt, work, wb, None)
+
+    assert bat(B=-1) == ESHAPE
+    assert bat(B=65536) == ESHAPE
+    assert bat(xr=511) == ESHAPE             # rows shorter than K
+    assert bat(ws=-4) == ESHAPE
+    assert bat(ws=6) == EALIGN               # weight matrices must stay 16-byte aligned
+    assert bat(bits=7) == EBITS
+    assert bat(K=500) == EGROUP
+    assert bat(B=0, w=None, x=None, o=None) == OK
+    assert bat(M=0, w=None, x=None, o=None) == OK
+    # workspace sizes: partials only when the plan splits, plus the copy of a misaligned x
+    wsb = L.qmx_qmm_batched_workspace_bytes
+    assert wsb(2, 4, 64, 512, 4, 64, BF16, FAKE, 2048, 512) == 0          # qmv route, aligned x
+    assert wsb(2, 4, 64, 512, 4, 64, BF16, ODD, 2048, 512) == 2 * 4 * 512 * 2
+    assert wsb(2, 4, 64, 512, 4, 64, BF16, FAKE, 2048, 513) == 2 * 4 * 512 * 2   # odd row stride
+
+
+def test_batched_plan_counts_every_problem():
+    # one problem of (M=16, N=256, K=4096) has 2 tiles: 16 partitions; 8 of them: 16 tiles, 16 partitions;
+    # 200 of them fill the chip without a split
+    assert qmx.plan_batched(1, 16, 256, 4096, 4, 64, BF16, 256) == qmx.plan(16, 256, 4096, 4, 64, BF16, 256)
+    r8, s8 = qmx.plan_batched(8, 16, 256, 4096, 4, 64, BF16, 256)
+    r1, s1 = qmx.plan_batched(1, 16, 256, 4096, 4, 64, BF16, 256)
+    assert r8 == r1 == "qmm_t_splitk" and s8 <= s1
+    assert qmx.plan_batched(200, 16, 256, 4096, 4, 64, BF16, 256) == ("qmm_t", 1)
+    assert qmx.plan_batched(8, 1, 4096, 4096, 4, 64, BF16, 256) == ("qmv", 1)

@@ -390,3 +390,75 @@ def test_large_n_and_m(orc):
     # widest configured row count on qmv and a large M on the matrix cores (sampled columns)
     check_affine(orc, "qmv", 1, 27648, 5120, 4, 64, qi.BF16, seed=1900, cols=sample_cols(27648, 512, 1))
     check_affine(orc, "qmm", 1024, 1024, 2048, 4, 64, qi.BF16, seed=1901, cols=sample_cols(1024, 128, 2))
+
+
+# ---------------------------------------------------------------- batched / strided / odd-offset activations
+def _batched_inputs(B, M, N, K, bits, gs, dt, seed, shared_w):
+    """B independent problems (each from its own seeded case, or one weight
+    set shared by all) as device tensors [B, ...] plus the per-problem cases."""
+    cases = [qi.affine_case(M, N, K, bits, gs, dt, seed=seed + (0 if shared_w else i)) for i in range(B)]
+    xs = [qi.affine_case(M, N, K, bits, gs, dt, seed=seed + 500 + i)["x"] for i in range(B)]
+    for c, x in zip(cases, xs):
+        c["x"] = x
+    if shared_w:
+        w, s, b, _ = to_dev(cases[0])
+    else:
+        parts = [to_dev(c) for c in cases]
+        w, s, b = (torch.stack([p[j] for p in parts]) for j in range(3))
+    x = torch.stack([qmx.storage_tensor(c["x"], dt, DEV) for c in cases])
+    return cases, w, s, b, x
+
+
+def _strided(x, kind):
+    """The same values as x [B, M, K] in a different layout: rows padded to a
+    wider (16-byte aligned) row, or shifted by one element (misaligned)."""
+    B, M, K = x.shape
+    if kind == "contiguous":
+        return x
+    pad = 64 if kind == "padded" else 1
+    big = torch.zeros((B, M, K + pad + 3), dtype=x.dtype, device=DEV)
+    off = 0 if kind == "padded" else 1
+    big[:, :, off:off + K] = x
+    v = big[:, :, off:off + K]
+    assert v.stride(1) == K + pad + 3 and (kind != "odd" or v.data_ptr() % 16 != 0)
+    return v
+
+
+@pytest.mark.parametrize("B,M,N,K,bits,gs,dt,shared,layout", [
+    (3, 1, 200, 1024, 4, 64, qi.BF16, False, "contiguous"),   # qmv route, one weight matrix per problem
+    (4, 3, 96, 512, 8, 32, qi.F32, True, "padded"),           # qmv route, f32, shared weights, padded rows
+    (3, 2, 130, 768, 6, 128, qi.F16, False, "odd"),            # qmv route, odd element offset (copied first)
+    (2, 37, 256, 2048, 3, 64, qi.F16, False, "padded"),        # matrix cores, 3-bit, padded rows
+    (2, 20, 384, 1024, 4, 64, qi.BF16, True, "odd"),           # matrix cores, odd offset (copied first)
+    (2, 16, 256, 4096, 4, 64, qi.BF16, False, "contiguous"),   # split-K across the batch
+    (3, 85, 128, 2560, 5, 32, qi.BF16, False, "odd"),          # two M tiles, split-K, odd offset
+])
+def test_batched_strided_and_odd_offset(orc, B, M, N, K, bits, gs, dt, shared, layout):
+    route = qmx.plan_batched(B, M, N, K, bits, gs, dt, 256)
+    say("batched", B, M, N, K, bits, gs, qi.DTYPE_NAMES[dt], shared, layout, route)
+    cases, w, s, b, x = _batched_inputs(B, M, N, K, bits, gs, dt, seed=2500 + B + M + bits, shared_w=shared)
+    xv = _strided(x, layout)
+    y = qmx.qmm_batched(w, s, b, xv, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    got = out64(y, dt)
+    for i, c in enumerate(cases):
+        ref = orc.affine(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs)
+        assert_close(got[i], ref, dt, orc, what=f"batched problem {i} of {B}, {layout}, route {route}")
+    # a second call on the same inputs gives the same bits
+    y2 = qmx.qmm_batched(w, s, b, xv, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16) if dt != qi.F32 else y.view(torch.int32),
+                       y2.view(torch.int16) if dt != qi.F32 else y2.view(torch.int32))
+
+
+def test_batched_single_problem_matches_unbatched(orc):
+    """A batch of one follows the unbatched plan and gives identical bits."""
+    for M, N, K in ((1, 200, 1024), (37, 256, 2048), (16, 256, 4096)):
+        say("batch of one", M, N, K)
+        c = qi.affine_case(M, N, K, 4, 64, qi.BF16, seed=2600 + M)
+        w, s, b, x = to_dev(c)
+        assert qmx.plan_batched(1, M, N, K, 4, 64, qi.BF16, 256) == qmx.plan(M, N, K, 4, 64, qi.BF16, 256)
+        y1 = qmx.qmm(w, s, b, x, bits=4, group_size=64)
+        yb = qmx.qmm_batched(w[None], s[None], b[None], x[None], bits=4, group_size=64)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), yb[0].view(torch.int16))
