@@ -251,6 +251,32 @@ size_t qmx_qmm_batched_workspace_bytes(int batch, int M, int N, int K, int bits,
                                        int dtype, const void* x, long long x_batch_stride,
                                        long long x_row_stride);
 
+/* qmx_qmm_gather -- qmx_qmm_batched where problem i takes weight matrix
+ * w_index[i] (of num_w) and activation matrix x_index[i] (of num_x) instead
+ * of matrix i (page "mlx PR 4682": gathered qmm, the batched route with
+ * per-problem weight selection, as mixture-of-experts layers use it).
+ *   out[i] = x_{x_index[i]} * dequant(W_{w_index[i]})^T,  i < batch
+ * w_index, x_index: device arrays of `batch` int32, 4-byte aligned, owned by
+ * the caller and read by the kernels (so not checked on the host): a value
+ * outside [0, count - 1] is clamped to that range.  Either may be NULL for
+ * the identity (then that operand has `batch` matrices).  Strides, layouts,
+ * routes, workspace (qmx_qmm_gather_workspace_bytes; a misaligned x is
+ * copied as num_x matrices) and errors as qmx_qmm_batched; QMX_ERR_SHAPE
+ * also for num_w or num_x < 1 with a non-empty batch.
+ */
+int qmx_qmm_gather(const uint32_t* w_packed, const void* scales, const void* biases,
+                   const void* x, void* out, const int32_t* w_index, const int32_t* x_index,
+                   int num_w, int num_x, int batch, int M, int N, int K,
+                   long long w_batch_stride, long long sb_batch_stride,
+                   long long x_batch_stride, long long x_row_stride, int bits, int group_size,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes qmx_qmm_gather needs (num_x: the activation matrices, or
+ * `batch` when x_index is NULL). */
+size_t qmx_qmm_gather_workspace_bytes(int batch, int num_x, int M, int N, int K, int bits,
+                                      int group_size, int dtype, const void* x,
+                                      long long x_batch_stride, long long x_row_stride);
+
 /* qmx_plan for a batch: the tiles of all problems share the device, so a
  * batch needs fewer K partitions.  Pure host function. */
 int qmx_plan_batched(int batch, int M, int N, int K, int bits, int group_size, int dtype,

@@ -51,6 +51,10 @@ _EXPORTS = {
     "qmx_qmm_batched_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 7 + [ctypes.c_void_p]
                                         + [ctypes.c_longlong] * 2),
     "qmx_plan_batched": (ctypes.c_int, [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_int)] * 2),
+    "qmx_qmm_gather": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 6 + [ctypes.c_longlong] * 4
+                       + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_qmm_gather_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 8 + [ctypes.c_void_p]
+                                       + [ctypes.c_longlong] * 2),
     "qmx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "qmx_api_version": (ctypes.c_int, []),
 }
@@ -317,6 +321,67 @@ def qmm_batched(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64,
     return out
 
 
+def gather_qmm(w_packed, scales, biases, x, w_index=None, x_index=None, out=None, *, bits=4, group_size=64,
+               workspace=None):
+    """Gathered quantized matmul (qmx_qmm_gather): out[i] = x[x_index[i]] @
+    dequant(W[w_index[i]]).T.  w_packed [E, N, K*bits/32] and scales/biases
+    [E, N, K/group_size] (each matrix contiguous); x [X, M, K] with a unit last
+    stride (any batch/row stride and offset); w_index, x_index: int32 device
+    vectors of one length B (None: identity, then that operand has B matrices);
+    out: contiguous [B, M, N]."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be [X, M, K] with a unit last stride")
+    if w_packed.dim() != 3 or scales.dim() != 3 or biases.dim() != 3:
+        raise ValueError("w_packed, scales and biases must be 3-D [E, ...]")
+    if w_packed.dtype not in _WORD_DTYPES:
+        raise ValueError("w_packed must hold uint32 words (torch.int32 or torch.uint32)")
+    X, M, K = x.shape
+    E, N, words = w_packed.shape
+    if words * 32 != K * bits:
+        raise ValueError(f"w_packed rows hold {words} words; K={K} at {bits} bits needs {K * bits / 32}")
+    G = K // group_size if group_size else 0
+    for name, t in (("scales", scales), ("biases", biases)):
+        if tuple(t.shape) != (E, N, G) or t.stride(2) != 1 or t.stride(1) != G:
+            raise ValueError(f"{name} must be [E, N, K/group_size] = {(E, N, G)} with contiguous matrices")
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype {x.dtype}")
+    if w_packed.stride(2) != 1 or w_packed.stride(1) != words:
+        raise ValueError("each matrix of w_packed must be contiguous")
+    if scales.stride(0) != biases.stride(0):
+        raise ValueError("scales and biases must share their batch stride")
+    lengths = {t.shape[0] for t in (w_index, x_index) if t is not None}
+    for t in (w_index, x_index):
+        if t is not None and (t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous()):
+            raise ValueError("indices must be contiguous int32 vectors")
+    if len(lengths) > 1:
+        raise ValueError("w_index and x_index must have one length")
+    B = lengths.pop() if lengths else E
+    if w_index is None and E != B:
+        raise ValueError("without w_index, w_packed must hold one matrix per problem")
+    if x_index is None and X != B:
+        raise ValueError("without x_index, x must hold one matrix per problem")
+    if out is None:
+        out = torch.empty((B, M, N), dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != (B, M, N) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [B, M, N] = {(B, M, N)} of dtype {x.dtype}")
+    for t in (w_packed, scales, biases, x, out, w_index, x_index):
+        if t is not None and (not t.is_cuda or t.device != x.device):
+            raise ValueError("all tensors must be on x's HIP device")
+    xs = x.stride(0) if X > 1 else 0
+    xr = x.stride(1) if M > 1 else K
+    dt = _dtype_code(x)
+    need = lib().qmx_qmm_gather_workspace_bytes(B, X, M, N, K, bits, group_size, dt, _ptr(x), xs, xr)
+    if need and workspace is None:
+        workspace = _workspace(x, need, None)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().qmx_qmm_gather(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), _ptr(w_index),
+                                _ptr(x_index), E, X, B, M, N, K, w_packed.stride(0) if E > 1 else 0,
+                                scales.stride(0) if E > 1 else 0, xs, xr, bits, group_size, dt, ws_ptr, ws_bytes,
+                                _stream(x)), "qmx_qmm_gather")
+    return out
+
+
 def _block_args(w_blocks, x, out, words_per_block, weights_per_block):
     if x.dim() != 1 or x.dtype != torch.float32:
         raise ValueError("x must be a float32 vector [K]")
@@ -373,7 +438,8 @@ def tensor_bits(t: torch.Tensor):
     return t.numpy()
 
 
-__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "qmm_batched", "plan", "plan_batched", "matvec_q8_0",
+__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "qmm_batched", "gather_qmm", "plan", "plan_batched",
+           "matvec_q8_0",
            "matvec_q4_k",
            "splitk_workspace_bytes", "qmm_workspace_bytes", "strerror", "api_version", "lib",
            "QmxError", "words_tensor", "storage_tensor", "tensor_bits",

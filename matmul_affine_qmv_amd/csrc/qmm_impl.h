@@ -249,11 +249,11 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
     using C = QmmCfg<DT, BITS, GS, MT, SBV>;
     // problem blockIdx.y of the batch (16-bit x, scales, biases and out)
-    const long long bz = blockIdx.y;
-    w += bz * sd.w;
-    scales = static_cast<const uint16_t*>(scales) + bz * sd.sb;
-    biases = static_cast<const uint16_t*>(biases) + bz * sd.sb;
-    x = static_cast<const uint16_t*>(x) + bz * sd.x;
+    const long long bz = blockIdx.y, wz = qmx_w_matrix(sd, bz), xz = qmx_x_matrix(sd, bz);
+    w += wz * sd.w;
+    scales = static_cast<const uint16_t*>(scales) + wz * sd.sb;
+    biases = static_cast<const uint16_t*>(biases) + wz * sd.sb;
+    x = static_cast<const uint16_t*>(x) + xz * sd.x;
     if constexpr (!SPLIT) out = static_cast<uint16_t*>(out) + bz * M * (long long)N;
     const long long XR = sd.x_row;
     constexpr int NB = QMM_NB;

@@ -437,11 +437,11 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     // problem blockIdx.z of the batch
     {
         constexpr int E = DT == DT_F32 ? 4 : 2;
-        const long long bz = blockIdx.z;
-        w += bz * sd.w;
-        scales = static_cast<const unsigned char*>(scales) + bz * sd.sb * E;
-        biases = static_cast<const unsigned char*>(biases) + bz * sd.sb * E;
-        x = static_cast<const unsigned char*>(x) + bz * sd.x * E;
+        const long long bz = blockIdx.z, wz = qmx_w_matrix(sd, bz), xz = qmx_x_matrix(sd, bz);
+        w += wz * sd.w;
+        scales = static_cast<const unsigned char*>(scales) + wz * sd.sb * E;
+        biases = static_cast<const unsigned char*>(biases) + wz * sd.sb * E;
+        x = static_cast<const unsigned char*>(x) + xz * sd.x * E;
         out = static_cast<unsigned char*>(out) + bz * M * (long long)N * E;
     }
     const int XR = (int)sd.x_row;

@@ -35,10 +35,27 @@ int qmm_mtiles_for(int M);
 // after the first (a stride of 0 shares that operand), x rows are `x_row`
 // elements apart (>= K), and it writes output matrix i of a contiguous
 // [batch][M][N] (split-K partials: [S][batch][M][N]).
+// With index arrays (gather), problem i takes weight matrix w_index[i] and x
+// matrix x_index[i] instead of i, each clamped to [0, count - 1].
 struct QmxStrides {
     long long w, sb, x, x_row;
+    const int* w_index = nullptr;
+    const int* x_index = nullptr;
+    int num_w = 0, num_x = 0;
 };
 inline QmxStrides unbatched(int K) { return QmxStrides{0, 0, 0, K}; }
+
+// Weight and x matrix of problem `i` (device side; a wave-uniform load).
+__device__ __forceinline__ long long qmx_w_matrix(const QmxStrides& sd, long long i) {
+    if (!sd.w_index) return i;
+    const int v = sd.w_index[i];
+    return v < 0 ? 0 : v >= sd.num_w ? sd.num_w - 1 : v;
+}
+__device__ __forceinline__ long long qmx_x_matrix(const QmxStrides& sd, long long i) {
+    if (!sd.x_index) return i;
+    const int v = sd.x_index[i];
+    return v < 0 ? 0 : v >= sd.num_x ? sd.num_x - 1 : v;
+}
 
 // M = 1 work split chosen for `rows` rows of W in all (N times the batch).
 struct QmvSplit {

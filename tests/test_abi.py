@@ -234,3 +234,17 @@ def test_batched_plan_counts_every_problem():
     assert r8 == r1 == "qmm_t_splitk" and s8 <= s1
     assert qmx.plan_batched(200, 16, 256, 4096, 4, 64, BF16, 256) == ("qmm_t", 1)
     assert qmx.plan_batched(8, 1, 4096, 4096, 4, 64, BF16, 256) == ("qmv", 1)
+
+
+@fake_ptr_test
+def test_gather_validation():
+    L = qmx.lib()
+
+    def gat(B=3, nw=2, nx=2, M=4, N=64, K=512, w=FAKE, x=FAKE, o=FAKE, wi=FAKE, xi=FAKE):
+        return L.qmx_qmm_gather(w, FAKE, FAKE, x, o, wi, xi, nw, nx, B, M, N, K, 128, 64, 2048, 512, 4, 64, BF16,
+                                None, 0, None)
+
+    assert gat(nw=0) == ESHAPE                # a non-empty batch needs at least one weight matrix
+    assert gat(nx=-1) == ESHAPE
+    assert gat(B=0, w=None, x=None, o=None, wi=None, xi=None) == OK
+    assert L.qmx_qmm_gather_workspace_bytes(3, 2, 4, 64, 512, 4, 64, BF16, ODD, 2048, 512) == 2 * 4 * 512 * 2

@@ -462,3 +462,42 @@ def test_batched_single_problem_matches_unbatched(orc):
         yb = qmx.qmm_batched(w[None], s[None], b[None], x[None], bits=4, group_size=64)
         torch.cuda.synchronize()
         assert torch.equal(y1.view(torch.int16), yb[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs,dt,layout", [
+    (1, 192, 1024, 4, 64, qi.BF16, "contiguous"),     # qmv route
+    (5, 160, 768, 3, 32, qi.F16, "odd"),             # qmv route, x copied first
+    (24, 256, 2048, 4, 64, qi.BF16, "padded"),        # matrix cores
+    (40, 128, 4096, 6, 128, qi.F16, "odd"),          # matrix cores, split-K, x copied first
+])
+def test_gather_qmm(orc, M, N, K, bits, gs, dt, layout):
+    """Problem i takes weight matrix w_index[i] and x matrix x_index[i] (repeated
+    and out-of-order picks); each output matches the oracle of its pair."""
+    E, X = 3, 2
+    w_index = [2, 0, 1, 1, 2, 0, 2]
+    x_index = [0, 1, 1, 0, 0, 1, 0]
+    B = len(w_index)
+    say("gather", M, N, K, bits, gs, qi.DTYPE_NAMES[dt], layout, qmx.plan_batched(B, M, N, K, bits, gs, dt, 256))
+    wc = [qi.affine_case(1, N, K, bits, gs, dt, seed=2700 + e) for e in range(E)]
+    xc = [qi.affine_case(M, 32, K, 4, gs, dt, seed=2750 + j)["x"] for j in range(X)]
+    parts = [to_dev(c) for c in wc]
+    w, s, b = (torch.stack([p[j] for p in parts]) for j in range(3))
+    x = _strided(torch.stack([qmx.storage_tensor(v, dt, DEV) for v in xc]), layout)
+    wi = torch.tensor(w_index, dtype=torch.int32, device=DEV)
+    xi = torch.tensor(x_index, dtype=torch.int32, device=DEV)
+    y = qmx.gather_qmm(w, s, b, x, wi, xi, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    got = out64(y, dt)
+    for i in range(B):
+        c = wc[w_index[i]]
+        ref = orc.affine(c["w"], c["scales"], c["biases"], dt, xc[x_index[i]], dt, M, N, K, bits, gs)
+        assert_close(got[i], ref, dt, orc, what=f"gather problem {i}: W{w_index[i]} x{x_index[i]}")
+    # indices outside the ranges are clamped: -3 -> 0, 99 -> E - 1 (and X - 1)
+    wi2 = torch.tensor([-3, 99, 1, 1, 2, 0, 2], dtype=torch.int32, device=DEV)
+    xi2 = torch.tensor([0, 1, 1, 0, 99, -1, 0], dtype=torch.int32, device=DEV)
+    y2 = qmx.gather_qmm(w, s, b, x, wi2, xi2, bits=bits, group_size=gs)
+    wi3 = torch.tensor([0, 2, 1, 1, 2, 0, 2], dtype=torch.int32, device=DEV)
+    xi3 = torch.tensor([0, 1, 1, 0, 1, 0, 0], dtype=torch.int32, device=DEV)
+    y3 = qmx.gather_qmm(w, s, b, x, wi3, xi3, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
