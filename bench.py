@@ -45,8 +45,9 @@ F32, F16, BF16 = 0, 1, 2
 DT_NAME = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 
-def affine(route, M, N, K, dt=BF16, bits=4, gs=64, B=1):
-    return {"kind": "affine", "route": route, "M": M, "N": N, "K": K, "bits": bits, "gs": gs, "dtype": dt, "B": B}
+def affine(route, M, N, K, dt=BF16, bits=4, gs=64, B=1, E=1):
+    return {"kind": "affine", "route": route, "M": M, "N": N, "K": K, "bits": bits, "gs": gs, "dtype": dt, "B": B,
+            "E": E}
 
 
 def block(kind, N, K):
@@ -73,6 +74,9 @@ WORKLOADS = {
     # illustrative shapes of the config-1 size class, not taken from the pages
     "batched_4bit_gs64_bf16": [affine("batched", 1, 4096, 4096, B=8), affine("batched", 16, 2048, 4096, B=8),
                                affine("batched", 56, 2048, 5120, B=4)],
+    # B problems gathering from E weight matrices (qmx_qmm_gather; every matrix is used, each by
+    # B/E problems), illustrative shapes as above
+    "gather_4bit_gs64_bf16": [affine("gather", 1, 2048, 4096, B=16, E=8), affine("gather", 16, 2048, 4096, B=16, E=8)],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
 }
@@ -82,6 +86,8 @@ DEFAULT_WORKLOAD = "qmv_qmm_4bit_gs64_bf16"
 def call_name(c):
     if c["kind"] == "affine":
         head = c["route"] if c.get("B", 1) == 1 else f"{c['route']}{c['B']}"
+        if c["route"] == "gather":
+            head += f"of{c['E']}"
         return f"{head}_M{c['M']}_N{c['N']}_K{c['K']}_b{c['bits']}_gs{c['gs']}_{DT_NAME[c['dtype']]}"
     return f"{c['kind']}_N{c['N']}_K{c['K']}"
 
@@ -95,6 +101,8 @@ def alg_bytes(c):
         return N * (K // 256) * 144 + 4 * K + 4 * N
     e = 4 if c["dtype"] == F32 else 2
     G = K // c["gs"]
+    if c["route"] == "gather":   # each of the E weight matrices is needed once; x and out per problem
+        return c["E"] * (N * K * c["bits"] // 8 + 2 * N * G * e) + c["B"] * (M * K * e + M * N * e)
     return c.get("B", 1) * (N * K * c["bits"] // 8 + 2 * N * G * e + M * K * e + M * N * e)
 
 
@@ -136,6 +144,20 @@ def make_inputs(c, seed, dev):
 
     import matmul_affine_qmv_amd as qmx
     import qmx_inputs as qi
+    if c["kind"] == "affine" and c["route"] == "gather":
+        parts = [qi.affine_case_torch(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"], seed + i, dev)
+                 for i in range(c["E"])]
+        d = {k: torch.stack([p[k] for p in parts]) for k in ("w", "scales", "biases")}
+        d["x"] = torch.stack([qi.affine_case_torch(c["M"], 32, c["K"], 4, c["gs"], c["dtype"], seed + 1000 + i,
+                                                   dev)["x"] for i in range(c["B"])])
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed)
+        d["w_index"] = (torch.randperm(c["B"], generator=g) % c["E"]).to(torch.int32).to(dev)
+        d["out"] = torch.empty((c["B"], c["M"], c["N"]), dtype=d["x"].dtype, device=dev)
+        need = qmx.lib().qmx_qmm_gather_workspace_bytes(c["B"], c["B"], c["M"], c["N"], c["K"], c["bits"], c["gs"],
+                                                         c["dtype"], d["x"].data_ptr(), c["M"] * c["K"], c["K"])
+        d["ws"] = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev) if need else None
+        return d
     if c["kind"] == "affine" and c["route"] == "batched":
         parts = [qi.affine_case_torch(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"], seed + i, dev)
                  for i in range(c["B"])]
@@ -171,6 +193,9 @@ def launch(c, d):
     if c["kind"] == "q4_k":
         return qmx.matvec_q4_k(d["blocks"], d["x"], d["out"])
     kw = dict(bits=c["bits"], group_size=c["gs"])
+    if c["route"] == "gather":
+        return qmx.gather_qmm(d["w"], d["scales"], d["biases"], d["x"], d["w_index"], None, d["out"],
+                              workspace=d["ws"], **kw)
     if c["route"] == "batched":
         return qmx.qmm_batched(d["w"], d["scales"], d["biases"], d["x"], d["out"], workspace=d["ws"], **kw)
     if c["route"] == "qmv":
@@ -243,9 +268,9 @@ def kernels_of(c, route, splits):
     """The kernels one call launches, each as (label, launcher over an input set,
     algorithmic bytes per launch, flops per launch, on the matrix cores)."""
     import matmul_affine_qmv_amd as qmx
-    if c["kind"] == "affine" and c["route"] == "batched":
+    if c["kind"] == "affine" and c["route"] in ("batched", "gather"):
         # one launch sequence for the whole batch, timed as a whole
-        return [("qmm_batched (whole call)", lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), c["M"] >= 8)]
+        return [(f"qmm_{c['route']} (whole call)", lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), c["M"] >= 8)]
     if c["kind"] != "affine" or route != "qmm_t_splitk":
         label = {"qmv": "qmv_kernel", "qmm_t": "qmm_t_kernel", "q8_0": "q8_0_kernel",
                  "q4_k": "q4_k_kernel"}[route if c["kind"] == "affine" else c["kind"]]
@@ -297,7 +322,9 @@ def cpu_baseline(calls, sets, target_s):
     for i, c in enumerate(calls):
         d = sets[0][i]
         if c.get("B", 1) > 1:   # a batch: the oracle takes its first problem
-            d = {k: v[0] for k, v in d.items() if k in ("w", "scales", "biases", "x", "out")}
+            wi = int(d["w_index"][0]) if "w_index" in d else 0
+            d = {k: v[wi if k in ("w", "scales", "biases") else 0] for k, v in d.items()
+                 if k in ("w", "scales", "biases", "x", "out")}
         h = {k: qmx.tensor_bits(d[k]) for k in ("w", "scales", "biases", "x", "blocks", "out") if k in d}
         if "w" in h:
             h["w"] = h["w"].view(np.uint32)
@@ -325,7 +352,7 @@ def cpu_baseline(calls, sets, target_s):
             ref = orc.q4_k(h["blocks"], h["x"], c["N"], c["K"], rows=cols)
         dt_s = time.perf_counter() - t0
         f_done = len(cols) / c["N"]
-        done_bytes += alg_bytes(c) / c.get("B", 1) * f_done
+        done_bytes += alg_bytes(dict(c, B=1, E=1, route="qmm")) * f_done
         done_s += dt_s
         if rate is None:
             rate = c["M"] * len(cols) * c["K"] / max(dt_s, 1e-6)
@@ -395,7 +422,7 @@ def main(argv=None):
         route, splits = c["route"], 1
         if c["kind"] == "affine" and route == "qmm":
             route, splits = qmx.plan(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"])
-        elif c["kind"] == "affine" and route == "batched":
+        elif c["kind"] == "affine" and route in ("batched", "gather"):
             route, splits = qmx.plan_batched(c["B"], c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"])
         shown = route if route != "qmm_t_splitk" else f"qmm_t_splitk{splits}"
         details.append({"call": call_name(c), "route": shown, "us": us, "alg_bytes": alg_bytes(c),
