@@ -49,11 +49,12 @@ class Oracle:
         lib.oracle_affine_hoisted.argtypes = [vp, vp, vp, ip, vp, ip, ip, ip, ip, ip, ip, dp]
         lib.oracle_q8_0.argtypes = [vp, vp, ip, ip, vp, ip, dp]
         lib.oracle_q4_k.argtypes = [vp, vp, ip, ip, vp, ip, dp]
+        lib.oracle_q8_i8.argtypes = [vp, vp, vp, ip, ip, vp, ip, dp]
         lib.oracle_round.argtypes = [dp, ctypes.c_long, ip, dp]
         lib.oracle_decode.argtypes = [vp, ctypes.c_long, ip, dp]
         lib.oracle_set_num_threads.argtypes = [ip]
         for name in ("oracle_affine_groups", "oracle_affine", "oracle_affine_hoisted",
-                     "oracle_q8_0", "oracle_q4_k", "oracle_round", "oracle_decode",
+                     "oracle_q8_0", "oracle_q4_k", "oracle_q8_i8", "oracle_round", "oracle_decode",
                      "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         lib.oracle_set_num_threads.restype = None
@@ -151,6 +152,19 @@ class Oracle:
         rc = self.lib.oracle_q4_k(self._p(blocks), self._p(x), N, K,
                                   None if rws is None else self._p(rws), nr, self._p(out))
         self._check(rc, "oracle_q4_k")
+        return out
+
+    def q8_i8(self, wq, xq, wd, N, K, rows=None):
+        """Integer-activation matvec: packed int8 weights and activations, float32 block scales."""
+        wq = self._c(wq, np.uint32)
+        xq = self._c(xq, np.uint32)
+        wd = self._c(wd, np.float32)
+        nr = N if rows is None else len(rows)
+        rws = None if rows is None else self._c(rows, np.int32)
+        out = np.empty(nr, dtype=np.float64)
+        rc = self.lib.oracle_q8_i8(self._p(wq), self._p(xq), self._p(wd), N, K,
+                                   None if rws is None else self._p(rws), nr, self._p(out))
+        self._check(rc, "oracle_q8_i8")
         return out
 
     # -------------------------------------------------------------- rounding

@@ -74,6 +74,24 @@ def q8_0_exact(blocks, x, N, K):
     return out
 
 
+def q8_i8_exact(wq, xq, wd, N, K):
+    """Integer-activation matvec in exact rationals, from the raw words: signed
+    bytes taken from each word's little-endian byte string."""
+    wq = np.asarray(wq, dtype=np.uint32).reshape(N, K // 4)
+    xbytes = b"".join(int(w).to_bytes(4, "little") for w in np.asarray(xq, dtype=np.uint32))
+    xv = [v - 256 if v >= 128 else v for v in xbytes]
+    scales = np.asarray(wd, dtype=np.float32).reshape(N, K // 32)
+    out = []
+    for n in range(N):
+        wbytes = b"".join(int(w).to_bytes(4, "little") for w in wq[n])
+        wv = [v - 256 if v >= 128 else v for v in wbytes]
+        tot = Fraction(0)
+        for b in range(K // 32):
+            tot += Fraction(float(scales[n, b])) * sum(wv[i] * xv[i] for i in range(32 * b, 32 * b + 32))
+        out.append(tot)
+    return out
+
+
 def q4_k_sub_scales(scale_bytes):
     """The eight (scale, min) 6-bit pairs of one Q4_K super-block.
 

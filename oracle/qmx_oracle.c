@@ -176,6 +176,38 @@ int oracle_q8_0(const uint32_t* blocks, const float* x, int N, int K,
     return 0;
 }
 
+/* Integer-activation matvec (page "hanzo-kernel src/quant.rs", packed-int8
+ * dp4a matvec and its block-per-row form): int8 weights wq[N][K] and int8
+ * activations xq[K], both packed four to a word (element i at byte i % 4 of
+ * word i / 4, two's complement), one float32 scale wd[n][b] per 32-element
+ * block:  out[n] = sum_b wd[n][b] * sum_{i in block b} wq[n][i] * xq[i].
+ * Each block's integer sum is exact in an int64; the scaled blocks are
+ * summed in float64. */
+static int sbyte(const uint32_t* wds, long i) {
+    unsigned v = (wds[i / 4] >> (8 * (i % 4))) & 0xFFu;
+    return v >= 128 ? (int)v - 256 : (int)v;
+}
+
+int oracle_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, int N, int K,
+                 const int32_t* rows, int nrows, double* out) {
+    if (N < 0 || K < 0 || K % 32) return -1;
+    int nb = K / 32;
+    int nr = rows ? nrows : N;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int r = 0; r < nr; ++r) {
+        int n = rows ? rows[r] : r;
+        const uint32_t* rw = wq + (long)n * (K / 4);
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) {
+            long long dot = 0;
+            for (int i = 32 * b; i < 32 * b + 32; ++i) dot += (long long)sbyte(rw, i) * sbyte(xq, i);
+            acc += (double)wd[(long)n * nb + b] * (double)dot;
+        }
+        out[r] = acc;
+    }
+    return 0;
+}
+
 /* Byte i of a little-endian sequence of words. */
 static unsigned byte_of(const uint32_t* wds, int i) {
     return (wds[i / 4] >> (8 * (i % 4))) & 0xFFu;

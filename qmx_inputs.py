@@ -166,6 +166,35 @@ def affine_case(M, N, K, bits, gs, dtype, seed, bias="jitter", x_dist="normal"):
     }
 
 
+# ---------------------------------------------------------------- int8 weights x int8 activations
+def pack_i8(q) -> np.ndarray:
+    """int8 values ``[..., 4n]`` -> uint32 words ``[..., n]`` (element i at byte i % 4)."""
+    return bytes_to_words(np.ascontiguousarray(np.asarray(q, dtype=np.int8)).view(np.uint8))
+
+
+def q8_i8_case(N, K, seed):
+    """Integer-activation matvec: int8 weights and activations uniform over all
+    256 values, float32 block scales U(0.001, 0.01)."""
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = random_bytes(rng, (N, K)).view(np.int8)
+    x = random_bytes(rng, (K,)).view(np.int8)
+    wd = rng.uniform(0.001, 0.01, size=(N, K // 32)).astype(np.float32)
+    return {"N": N, "K": K, "q": q, "xq_values": x, "wq": pack_i8(q), "xq": pack_i8(x), "wd": wd, "seed": seed}
+
+
+def q8_i8_case_torch(N, K, seed, device):
+    """The same distributions drawn on a torch device (seeded Philox)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    wq = torch.randint(-(2 ** 31), 2 ** 31, (N, K // 4), dtype=torch.int64, generator=g, device=device).to(torch.int32)
+    xq = torch.randint(-(2 ** 31), 2 ** 31, (K // 4,), dtype=torch.int64, generator=g, device=device).to(torch.int32)
+    wd = torch.rand((N, K // 32), generator=g, device=device, dtype=torch.float32) * 0.009 + 0.001
+    return {"N": N, "K": K, "wq": wq, "xq": xq, "wd": wd, "seed": seed}
+
+
 # ---------------------------------------------------------------- Q8_0
 def q8_0_case(N, K, seed):
     """Q8_0 matvec: quants U{-127..127}, f16 block scale U(0.001, 0.01), x ~ N(0,1) f32."""

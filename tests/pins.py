@@ -166,6 +166,40 @@ def pin_q4_k_brute(o):
         assert _rel_err(got, ex) < 1e-14
 
 
+def pin_q8_i8_brute(o):
+    for i, (N, K) in enumerate([(1, 32), (3, 64), (2, 128)]):
+        c = qi.q8_i8_case(N, K, seed=965 + i)
+        got = o.q8_i8(c["wq"], c["xq"], c["wd"], N, K)
+        ex = brute.q8_i8_exact(c["wq"], c["xq"], c["wd"], N, K)
+        assert _rel_err(got, ex) < 1e-14
+
+
+def pin_q8_i8_layout(o):
+    """One-hot activations read single weights back through the packed layout."""
+    g = _golden("int8_layout.json")
+    for case in g["cases"]:
+        words = np.array([int(w, 16) for w in case["words"]], dtype=np.uint32)
+        K = 4 * len(words)
+        Kp = 32 * ((K + 31) // 32)
+        wq = np.zeros((1, Kp // 4), dtype=np.uint32)
+        wq[0, :len(words)] = words
+        wd = np.ones((1, Kp // 32), dtype=np.float32)
+        for i, v in enumerate(case["values"]):
+            onehot = np.zeros(Kp, dtype=np.int8)
+            onehot[i] = 1
+            got = o.q8_i8(wq, qi.pack_i8(onehot), wd, 1, Kp)[0]
+            assert got == v, (case, i, got)
+
+
+def pin_q8_i8_integer_gemv(o):
+    """Unit block scales: the exact integer matrix-vector product (numpy int64)."""
+    c = qi.q8_i8_case(7, 256, seed=968)
+    ones = np.ones_like(c["wd"])
+    got = o.q8_i8(c["wq"], c["xq"], ones, 7, 256)
+    want = c["q"].astype(np.int64) @ c["xq_values"].astype(np.int64)
+    assert np.array_equal(got, want.astype(np.float64))
+
+
 # ---------------------------------------------------------------- identities and library routines
 def pin_dense_numpy(o):
     """Dequantise from the raw codes with numpy, then x @ W.T in float64."""
@@ -281,6 +315,7 @@ def pin_q4_k_dense(o):
 
 
 ALL_PINS = [pin_layouts, pin_half_decode, pin_rounding, pin_q8_0_golden, pin_q4_k_golden,
+            pin_q8_i8_brute, pin_q8_i8_layout, pin_q8_i8_integer_gemv,
             pin_affine_brute, pin_q8_0_brute, pin_q4_k_brute, pin_dense_numpy, pin_hoist_identity,
             pin_special_cases, pin_split_additivity, pin_columns_subset, pin_q8_0_dense,
             pin_q4_k_dense]

@@ -22,6 +22,9 @@ MUTANTS = {
                            "acc += value_at(x, x_dt, (size_t)k * M + m) * wk;"),
     "scale_bias_swapped": ("double wk = value_at(s, sb_dt, (size_t)n * G + g) * (double)code_at(row, k, bits)\n                      + value_at(b, sb_dt, (size_t)n * G + g);",
                            "double wk = value_at(b, sb_dt, (size_t)n * G + g) * (double)code_at(row, k, bits)\n                      + value_at(s, sb_dt, (size_t)n * G + g);"),
+    "i8_no_sign_extension": ("return v >= 128 ? (int)v - 256 : (int)v;", "return (int)v;"),
+    "i8_block_scale_shifted": ("acc += (double)wd[(long)n * nb + b] * (double)dot;",
+                               "acc += (double)wd[(long)n * nb + (b + 1) % nb] * (double)dot;"),
     "q8_no_sign_extension": ("int q = byte >= 128 ? (int)byte - 256 : (int)byte;", "int q = (int)byte;"),
     "q8_scale_high_half": ("double d = dec_f16((uint16_t)(blk[0] & 0xFFFFu));",
                            "double d = dec_f16((uint16_t)(blk[0] >> 16));"),
