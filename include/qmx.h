@@ -181,6 +181,21 @@ int qmx_matvec_q8_0(const uint32_t* w_blocks, const float* x, float* out, int N,
 int qmx_matvec_q4_k(const uint32_t* w_blocks, const float* x, float* out, int N, int K,
                     void* stream);
 
+/* qmx_matvec_q8_i8 -- integer-activation matvec (page "hanzo-kernel
+ * src/quant.rs", packed-int8 dp4a matvec and its block-per-row form):
+ *   out[n] = sum_b wd[n*K/32 + b] * sum_{i in block b} wq[n][i] * xq[i]
+ * wq: int8 weights [N][K] packed four to a uint32 (element i at byte i % 4,
+ * two's complement); xq: int8 activations [K] packed the same way; wd:
+ * float32 [N][K/32], one scale per 32-element block of a row; out: float32
+ * [N].  Each block's integer sum is exact (4-way integer dot instructions);
+ * the scaled blocks are summed in float32.  Requirements: K % 32 == 0
+ * (QMX_ERR_GROUP), wq and xq 16-byte aligned, wd and out 4-byte aligned
+ * (QMX_ERR_ALIGN); K = 0 writes zeros.  Device pointers, caller-owned,
+ * asynchronous on `stream`.
+ */
+int qmx_matvec_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, float* out,
+                     int N, int K, void* stream);
+
 /* qmx_plan -- the dispatch policy as a pure host function (page "mlx PR
  * 4682", dispatch table and split rule; page "metaltile-std
  * src/mlx/quantized.rs", M-based kernel selector).  Writes the route

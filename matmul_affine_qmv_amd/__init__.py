@@ -42,6 +42,7 @@ _EXPORTS = {
     "qmx_splitk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
     "qmx_matvec_q8_0": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
     "qmx_matvec_q4_k": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
+    "qmx_matvec_q8_i8": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
     "qmx_plan": (ctypes.c_int, [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_int)] * 2),
     "qmx_qmm_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 6),
     "qmx_qmm": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
@@ -413,6 +414,25 @@ def matvec_q4_k(w_blocks, x, out=None):
     return out
 
 
+def matvec_q8_i8(wq, xq, wd, out=None):
+    """Integer-activation matvec: wq [N, K/4] and xq [K/4] int32 words holding
+    four int8 each, wd float32 [N, K/32]; out float32 [N]."""
+    if wq.dim() != 2 or xq.dim() != 1 or wq.dtype not in _WORD_DTYPES or xq.dtype not in _WORD_DTYPES:
+        raise ValueError("wq must be [N, K/4] and xq [K/4] uint32 words (torch.int32 or torch.uint32)")
+    N, K = wq.shape[0], 4 * xq.shape[0]
+    if wq.shape[1] * 4 != K:
+        raise ValueError("wq rows and xq must hold the same K")
+    if wd.dtype != torch.float32 or tuple(wd.shape) != (N, K // 32):
+        raise ValueError(f"wd must be float32 [N, K/32] = {(N, K // 32)}")
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=xq.device)
+    elif tuple(out.shape) != (N,) or out.dtype != torch.float32:
+        raise ValueError("out must be a float32 vector [N]")
+    _need_cuda(wq, xq, wd, out)
+    _check(lib().qmx_matvec_q8_i8(_ptr(wq), _ptr(xq), _ptr(wd), _ptr(out), N, K, _stream(xq)), "qmx_matvec_q8_i8")
+    return out
+
+
 def words_tensor(a, device) -> torch.Tensor:
     """numpy uint32 array -> int32 tensor with the same bits on `device`."""
     import numpy as np
@@ -440,7 +460,7 @@ def tensor_bits(t: torch.Tensor):
 
 __all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "qmm_batched", "gather_qmm", "plan", "plan_batched",
            "matvec_q8_0",
-           "matvec_q4_k",
+           "matvec_q4_k", "matvec_q8_i8",
            "splitk_workspace_bytes", "qmm_workspace_bytes", "strerror", "api_version", "lib",
            "QmxError", "words_tensor", "storage_tensor", "tensor_bits",
            "QMX_F32", "QMX_F16", "QMX_BF16"]

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqmx.so")
 
 SOURCES = ["qmv.hip", "qmm_b4.hip", "qmm_b8.hip", "qmm_b2.hip", "qmm_b3.hip", "qmm_b6.hip", "qmm_b5.hip",
-           "qmm_b1.hip", "blocks.hip", "qmm.hip", "qmx_api.cpp"]
+           "qmm_b1.hip", "blocks.hip", "q8_i8.hip", "qmm.hip", "qmx_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are kept out of every device build.

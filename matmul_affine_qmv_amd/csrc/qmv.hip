@@ -151,14 +151,6 @@ struct QmvStage {
     u32x4 x[MT][XQ];
 };
 
-// Buffer resource over [p, p + bytes) (bytes clamped to 32 bits); every offset
-// used below stays inside the array, so the range check never trims a load.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, size_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
-                                             (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes),
-                                             0x00020000);
-}
-
 template <int DT>
 __device__ __forceinline__ uint32_t buffer_raw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     if constexpr (DT == DT_F32) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);

@@ -231,6 +231,19 @@ int qmx_matvec_q4_k(const uint32_t* w_blocks, const float* x, float* out, int N,
     return launch_status(qmx::launch_q4_k(w_blocks, x, out, N, K, static_cast<hipStream_t>(stream)));
 }
 
+int qmx_matvec_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, float* out, int N, int K,
+                     void* stream) {
+    if (N < 0 || K < 0) return QMX_ERR_SHAPE;
+    if (K % 32 != 0) return QMX_ERR_GROUP;
+    // per-lane offsets of one work-group's rows stay in 32 bits
+    if ((long long)16 * K > INT_MAX) return QMX_ERR_SHAPE;
+    if (N == 0) return QMX_OK;
+    if (!out || (K > 0 && (!wq || !xq || !wd))) return QMX_ERR_NULL;
+    if (!is_aligned(out, 4) || (K > 0 && (!is_aligned(wq, 16) || !is_aligned(xq, 16) || !is_aligned(wd, 4))))
+        return QMX_ERR_ALIGN;
+    return launch_status(qmx::launch_q8_i8(wq, xq, wd, out, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus, int* route, int* splits) {
     if (!route || !splits) return QMX_ERR_NULL;
     return plan_impl(M, N, K, bits, group_size, dtype, num_cus, route, splits);

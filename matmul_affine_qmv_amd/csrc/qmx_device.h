@@ -67,6 +67,15 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
     return DT == DT_F16 ? f16_bits_to_f32(w >> 16) : __uint_as_float(w & 0xffff0000u);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Buffer resource over [p, p + bytes) (bytes clamped to 32 bits); the kernels
+// keep every offset inside the array, so the range check never trims a load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                             (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes),
+                                             0x00020000);
+}
+
 // ---------------------------------------------------------------- code pairs
 // The magic exponent bytes above a pair of 16-bit codes (0x43 for bf16: the
 // value 128 + q; 0x64 for f16: 1024 + q) as an opaque register value.  With

@@ -83,5 +83,7 @@ hipError_t launch_splitk_accum(const float* ws, void* out, int splits, size_t MN
 
 hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st);
 hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st);
+hipError_t launch_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, float* out, int N, int K,
+                        hipStream_t st);
 
 }  // namespace qmx

@@ -248,3 +248,14 @@ def test_gather_validation():
     assert gat(nx=-1) == ESHAPE
     assert gat(B=0, w=None, x=None, o=None, wi=None, xi=None) == OK
     assert L.qmx_qmm_gather_workspace_bytes(3, 2, 4, 64, 512, 4, 64, BF16, ODD, 2048, 512) == 2 * 4 * 512 * 2
+
+
+@fake_ptr_test
+def test_q8_i8_validation():
+    f = qmx.lib().qmx_matvec_q8_i8
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 48, None) == EGROUP      # K not a multiple of 32
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 64, None) == ESHAPE
+    assert f(ODD, FAKE, FAKE, FAKE, 8, 64, None) == EALIGN       # packed weights need 16-byte alignment
+    assert f(FAKE, FAKE, ctypes.c_void_p(0x10001), FAKE, 8, 64, None) == EALIGN
+    assert f(FAKE, None, FAKE, FAKE, 8, 64, None) == ENULL
+    assert f(None, None, None, FAKE, 0, 64, None) == OK          # empty output

@@ -501,3 +501,45 @@ def test_gather_qmm(orc, M, N, K, bits, gs, dt, layout):
     y3 = qmx.gather_qmm(w, s, b, x, wi3, xi3, bits=bits, group_size=gs)
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
+
+
+# ---------------------------------------------------------------- integer activations
+def _q8_i8_dev(c):
+    return (qmx.words_tensor(c["wq"], DEV), qmx.words_tensor(c["xq"], DEV),
+            torch.from_numpy(np.ascontiguousarray(c["wd"])).to(DEV))
+
+
+@pytest.mark.parametrize("N,K", [(14336, 5120), (1, 32), (7, 256), (33, 1312), (130, 4096)])
+def test_q8_i8_matvec(orc, N, K):
+    say("q8_i8", N, K)
+    c = qi.q8_i8_case(N, K, seed=3000 + N + K)
+    wq, xq, wd = _q8_i8_dev(c)
+    y = qmx.matvec_q8_i8(wq, xq, wd)
+    torch.cuda.synchronize()
+    ref = orc.q8_i8(c["wq"], c["xq"], c["wd"], N, K)
+    assert_close(y.cpu().numpy().astype(np.float64), ref, qi.F32, orc, what=f"q8_i8 {N}x{K}")
+    y2 = qmx.matvec_q8_i8(wq, xq, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_q8_i8_integer_exact_and_empty(orc):
+    """Unit block scales: every partial sum is an integer below 2^24, so the
+    float32 result equals the exact integer product bit for bit; K = 0 gives zeros."""
+    N, K = 300, 1024
+    say("q8_i8 unit scales", N, K)
+    c = qi.q8_i8_case(N, K, seed=3100)
+    c["wd"] = np.ones_like(c["wd"])
+    wq, xq, wd = _q8_i8_dev(c)
+    y = qmx.matvec_q8_i8(wq, xq, wd)
+    torch.cuda.synchronize()
+    want = c["q"].astype(np.int64) @ c["xq_values"].astype(np.int64)
+    assert np.array_equal(y.cpu().numpy().astype(np.int64), want)
+    assert np.array_equal(orc.q8_i8(c["wq"], c["xq"], c["wd"], N, K), want.astype(np.float64))
+    say("q8_i8 K=0")
+    y0 = qmx.matvec_q8_i8(torch.zeros((5, 0), dtype=torch.int32, device=DEV),
+                          torch.zeros(0, dtype=torch.int32, device=DEV),
+                          torch.zeros((5, 0), dtype=torch.float32, device=DEV),
+                          torch.full((5,), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, torch.zeros(5, device=DEV))
