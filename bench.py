@@ -78,6 +78,7 @@ WORKLOADS = {
     # B/E problems), illustrative shapes as above
     "gather_4bit_gs64_bf16": [affine("gather", 1, 2048, 4096, B=16, E=8), affine("gather", 16, 2048, 4096, B=16, E=8)],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
+    "q8_i8_14336x5120": [block("q8_i8", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
 }
 DEFAULT_WORKLOAD = "qmv_qmm_4bit_gs64_bf16"
@@ -99,6 +100,8 @@ def alg_bytes(c):
         return N * (K // 32) * 36 + 4 * K + 4 * N
     if c["kind"] == "q4_k":
         return N * (K // 256) * 144 + 4 * K + 4 * N
+    if c["kind"] == "q8_i8":   # int8 weights, float32 block scales, int8 x, float32 out
+        return N * K + N * (K // 32) * 4 + K + 4 * N
     e = 4 if c["dtype"] == F32 else 2
     G = K // c["gs"]
     if c["route"] == "gather":   # each of the E weight matrices is needed once; x and out per problem
@@ -175,6 +178,10 @@ def make_inputs(c, seed, dev):
             need = qmx.qmm_workspace_bytes(c["M"], c["N"], c["K"], c["bits"], c["gs"], c["dtype"])
         d["ws"] = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev) if need else None
         return d
+    if c["kind"] == "q8_i8":
+        d = qi.q8_i8_case_torch(c["N"], c["K"], seed, dev)
+        d["out"] = torch.empty(c["N"], dtype=torch.float32, device=dev)
+        return d
     gen = qi.q8_0_case_torch if c["kind"] == "q8_0" else qi.q4_k_case_torch
     d = gen(c["N"], c["K"], seed, dev)
     d["out"] = torch.empty(c["N"], dtype=torch.float32, device=dev)
@@ -182,7 +189,7 @@ def make_inputs(c, seed, dev):
 
 
 def footprint(c, d):
-    keys = ("w", "scales", "biases", "x", "blocks")
+    keys = ("w", "scales", "biases", "x", "blocks", "wq", "xq", "wd")
     return sum(d[k].numel() * d[k].element_size() for k in keys if k in d)
 
 
@@ -192,6 +199,8 @@ def launch(c, d):
         return qmx.matvec_q8_0(d["blocks"], d["x"], d["out"])
     if c["kind"] == "q4_k":
         return qmx.matvec_q4_k(d["blocks"], d["x"], d["out"])
+    if c["kind"] == "q8_i8":
+        return qmx.matvec_q8_i8(d["wq"], d["xq"], d["wd"], d["out"])
     kw = dict(bits=c["bits"], group_size=c["gs"])
     if c["route"] == "gather":
         return qmx.gather_qmm(d["w"], d["scales"], d["biases"], d["x"], d["w_index"], None, d["out"],
@@ -273,7 +282,7 @@ def kernels_of(c, route, splits):
         return [(f"qmm_{c['route']} (whole call)", lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), c["M"] >= 8)]
     if c["kind"] != "affine" or route != "qmm_t_splitk":
         label = {"qmv": "qmv_kernel", "qmm_t": "qmm_t_kernel", "q8_0": "q8_0_kernel",
-                 "q4_k": "q4_k_kernel"}[route if c["kind"] == "affine" else c["kind"]]
+                 "q4_k": "q4_k_kernel", "q8_i8": "q8_i8_kernel"}[route if c["kind"] == "affine" else c["kind"]]
         return [(label, lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), route == "qmm_t")]
     M, N, K, e = c["M"], c["N"], c["K"], 2
     parts = splits * M * N * 4
@@ -325,11 +334,11 @@ def cpu_baseline(calls, sets, target_s):
             wi = int(d["w_index"][0]) if "w_index" in d else 0
             d = {k: v[wi if k in ("w", "scales", "biases") else 0] for k, v in d.items()
                  if k in ("w", "scales", "biases", "x", "out")}
-        h = {k: qmx.tensor_bits(d[k]) for k in ("w", "scales", "biases", "x", "blocks", "out") if k in d}
-        if "w" in h:
-            h["w"] = h["w"].view(np.uint32)
-        if "blocks" in h:
-            h["blocks"] = h["blocks"].view(np.uint32)
+        h = {k: qmx.tensor_bits(d[k]) for k in ("w", "scales", "biases", "x", "blocks", "wq", "xq", "wd", "out")
+             if k in d}
+        for k in ("w", "blocks", "wq", "xq"):
+            if k in h:
+                h[k] = h[k].view(np.uint32)
         host.append(h)
     macs = [c["M"] * c["N"] * c["K"] for c in calls]
     # probe the oracle's rate on a small slice of the first call
@@ -348,6 +357,8 @@ def cpu_baseline(calls, sets, target_s):
                              c["K"], c["bits"], c["gs"], cols=cols)
         elif c["kind"] == "q8_0":
             ref = orc.q8_0(h["blocks"], h["x"], c["N"], c["K"], rows=cols)
+        elif c["kind"] == "q8_i8":
+            ref = orc.q8_i8(h["wq"], h["xq"], h["wd"], c["N"], c["K"], rows=cols)
         else:
             ref = orc.q4_k(h["blocks"], h["x"], c["N"], c["K"], rows=cols)
         dt_s = time.perf_counter() - t0
