@@ -70,6 +70,9 @@ WORKLOADS = {
     "qmv_4bit_gs64_f32_4096": [affine("qmv", 1, 4096, 4096, F32)],
     "qmm_4bit_gs64_bf16": [affine("qmm", m, n, k) for k, n, m in QMM_SHAPES],
     "qmm_control_4096_m512": [affine("qmm", 512, 4096, 4096)],
+    # the compute-bound regime: larger M on the same weights (illustrative sizes)
+    "qmm_large_m_4bit_gs64_bf16": [affine("qmm", m, n, k) for k, n, m in
+                                   ((4096, 4096, 512), (4096, 4096, 1024), (4096, 4096, 2048), (4096, 14336, 1024))],
     # batches of independent problems, each with its own weights (qmx_qmm_batched):
     # illustrative shapes of the config-1 size class, not taken from the pages
     "batched_4bit_gs64_bf16": [affine("batched", 1, 4096, 4096, B=8), affine("batched", 16, 2048, 4096, B=8),
