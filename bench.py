@@ -68,6 +68,8 @@ WORKLOADS = {
     "qmv_4bit_gs64_f16": [affine("qmv", 1, n, k, F16) for n, k in QMV_SHAPES],
     "qmv_4bit_gs64_f32": [affine("qmv", 1, n, k, F32) for n, k in QMV_SHAPES],
     "qmv_4bit_gs64_f32_4096": [affine("qmv", 1, 4096, 4096, F32)],
+    # small decode batches (M = 2..7 rows of x share each weight read)
+    "qmv_small_m_4bit_gs64_bf16": [affine("qmv", m, n, k) for m in (2, 4, 7) for n, k in ((4096, 4096), (14336, 5120))],
     "qmm_4bit_gs64_bf16": [affine("qmm", m, n, k) for k, n, m in QMM_SHAPES],
     "qmm_control_4096_m512": [affine("qmm", 512, 4096, 4096)],
     # the compute-bound regime: larger M on the same weights (illustrative sizes)

@@ -97,7 +97,8 @@ int qmx_qmv(const uint32_t* w_packed, const void* scales, const void* biases,
             const void* x, void* out, int M, int N, int K, int bits, int group_size,
             int dtype, void* stream);
 
-/* qmx_qmm_t -- affine quantized x * W^T for M >= 8 on the matrix cores
+/* qmx_qmm_t -- affine quantized x * W^T on the matrix cores (any M; built
+ * for M >= 8, and what qmx_plan picks at M = 2..7 for large weights)
  * (page "mlx PR 4682": staged transposed qmm that fetches the next K step
  * while the current one is consumed from threadgroup memory, with one
  * barrier per K step).  Here the packed codes and x of the next K blocks are
@@ -201,7 +202,11 @@ int qmx_matvec_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, fl
  * src/mlx/quantized.rs", M-based kernel selector).  Writes the route
  * (qmx_route) and split count (1 when unsplit) that qmx_qmm would use for
  * this problem on a device with `num_cus` compute units (num_cus <= 0:
- * 256).  Performs no HIP call.  Returns QMX_OK or a validation status.
+ * 256).  Routes: float32 activations, K % 128 != 0 and M = 1 take qmx_qmv;
+ * M = 2..7 takes qmx_qmv unless a cost estimate (qmv's vector work grows
+ * with M, the matrix route with the weight bytes) favours the matrix cores;
+ * otherwise qmx_qmm_t, split along K when its tiles leave compute units idle.
+ * Performs no HIP call.  Returns QMX_OK or a validation status.
  * route/splits: host pointers.
  */
 int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus,

@@ -3,6 +3,7 @@
 // HIP call, so argument errors never reach the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -92,13 +93,32 @@ int device_cus() {
     return cus;
 }
 
+// Below M = 8 qmv reads each weight once for up to 4 rows of x, but its vector
+// work grows with M: about 1.125 + 0.5 * m instructions per code for a pass
+// over m <= 4 rows (code expansion plus one dot2 per pair and row), and a
+// second pass for M > 4.  The matrix route costs about its weight bytes at
+// 2.3 TB/s with a floor of about 9 us; qmv has a floor of about 5.5 us and
+// about 8.9e-8 us per code and instruction.  Measured on the chip at N x K =
+// 4096 x 4096 and 14336 x 5120 for M = 2..7: qmv stays ahead on the smaller
+// matrix up to M = 5, the matrix route from M = 4 on the larger one.
+bool small_m_prefers_matrix(int M, int N, int K, int bits, int batch) {
+    if (M < 2 || M >= 8) return false;
+    const double codes = (double)N * K * (batch > 0 ? batch : 1);
+    const int first = M < 4 ? M : 4, second = M - first;
+    const double per_code = 1.125 + 0.5 * first + (second > 0 ? 1.125 + 0.5 * second : 0.0);
+    const double t_qmv = std::max(5.5, 8.9e-8 * codes * per_code);
+    const double t_mat = std::max(9.0, codes * bits / 8.0 / 2.3e6);
+    return t_mat < t_qmv;
+}
+
 int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int* route, int* splits,
               int batch = 1) {
     int rc = check_affine_common(M, N, K, bits, gs, dtype);
     if (rc) return rc;
     if (num_cus <= 0) num_cus = kDefaultCUs;
-    // float32, M < 8 and K that the staged kernel cannot block stay on qmv.
-    if (dtype == QMX_F32 || M < 8 || K % QMM_KB != 0) {
+    // float32, K that the staged kernel cannot block and M < 8 stay on qmv,
+    // unless M is 2..7 and the vector-ALU work of qmv outweighs the matrix route.
+    if (dtype == QMX_F32 || K % QMM_KB != 0 || (M < 8 && !small_m_prefers_matrix(M, N, K, bits, batch))) {
         if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
         *route = QMX_ROUTE_QMV;
         *splits = 1;

@@ -172,6 +172,13 @@ def test_block_validation():
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
     (8, 4096, 4096, F16, "qmm_t_splitk", 8),
     (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
+    (2, 14336, 5120, BF16, "qmv", 1),                # M = 2..7: qmv while its vector work is small
+    (4, 14336, 5120, BF16, "qmm_t_splitk", 2),       # ... the matrix route once it is not
+    (7, 27648, 5120, BF16, "qmm_t", 1),
+    (5, 5120, 5120, F16, "qmm_t_splitk", 6),
+    (4, 5120, 5120, BF16, "qmv", 1),
+    (7, 2048, 2048, BF16, "qmv", 1),
+    (7, 14336, 5120, F32, "qmv", 1),                 # float32 stays on qmv at every M
 ])
 def test_plan_table(M, N, K, dtype, route, splits):
     assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)

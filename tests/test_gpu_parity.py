@@ -134,9 +134,16 @@ def test_qmv_config2_full(orc, NK, dt):
 
 
 # ---------------------------------------------------------------- qmm_t and split-K
-@pytest.mark.parametrize("M", [8, 9, 16, 22, 33, 56, 85, 128, 129, 200])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 7, 8, 9, 16, 22, 33, 56, 85, 128, 129, 200])
 def test_qmm_t_small_m_tails(orc, M):
     check_affine(orc, "qmm_t", M, 200, 512, 4, 64, qi.BF16, seed=1200 + M)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 14336, 5120), (7, 27648, 5120), (5, 5120, 5120)])
+def test_small_m_matrix_route(orc, M, N, K):
+    """M < 8 shapes that the policy sends to the matrix cores (sampled columns)."""
+    assert qmx.plan(M, N, K, 4, 64, qi.BF16)[0] != "qmv"
+    check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=1250 + M, cols=sample_cols(N, 256, M), reruns=1)
 
 
 @pytest.mark.parametrize("bits", ALL_BITS)
