@@ -550,3 +550,32 @@ def test_q8_i8_integer_exact_and_empty(orc):
                           torch.full((5,), 7.0, device=DEV))
     torch.cuda.synchronize()
     assert torch.equal(y0, torch.zeros(5, device=DEV))
+
+
+# ---------------------------------------------------------------- seeded random sweep
+def _random_cases(n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        bits = int(rng.choice(ALL_BITS))
+        gs = int(rng.choice([32, 64, 128]))
+        dt = int(rng.choice([qi.F32, qi.F16, qi.BF16]))
+        M = int(rng.choice([1, 2, 3, 4, 6, 7, 8, 13, 24, 40, 65, 97, 150]))
+        N = int(rng.integers(1, 700))
+        K = 128 * int(rng.integers(1, 40))
+        route = "qmm" if dt == qi.F32 or rng.random() < 0.5 else str(rng.choice(["qmv", "qmm_t", "splitk"]))
+        if route == "splitk" and K // 256 < 2:
+            route = "qmm_t"
+        out.append((i, M, N, K, bits, gs, dt, route))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(40, 4242), ids=lambda c: f"r{c[0]}")
+def test_random_sweep(orc, case):
+    """Seeded random shapes, code widths, group sizes, dtypes and routes (ragged N,
+    every M tile count), each against the oracle on all outputs."""
+    i, M, N, K, bits, gs, dt, route = case
+    splits = None
+    if route == "splitk":
+        splits = int(np.random.Generator(np.random.PCG64(i)).integers(2, min(16, K // 256) + 1))
+    check_affine(orc, route, M, N, K, bits, gs, dt, seed=5000 + i, splits=splits)
