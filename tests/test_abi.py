@@ -162,7 +162,9 @@ def test_block_validation():
     (7, 4096, 4096, BF16, "qmv", 1),
     (16, 4096, 4096, F32, "qmv", 1),                 # float32 never takes the matrix cores
     (16, 4096, 4096, BF16, "qmm_t_splitk", 8),       # 32 tiles on 256 CUs
-    (16, 4096, 256, BF16, "qmm_t", 1),               # K < 512 stays unsplit
+    (16, 4096, 256, BF16, "qmm_t", 1),               # K < 1024 stays unsplit
+    (16, 4096, 768, BF16, "qmm_t", 1),
+    (16, 4096, 1024, BF16, "qmm_t_splitk", 4),       # capped at K / 256 partitions
     (22, 2048, 2048, BF16, "qmm_t_splitk", 8),       # capped at K / 256 partitions
     (85, 2048, 10752, BF16, "qmm_t_splitk", 8),       # 2 M tiles of 43 rows x 16 N tiles
     (128, 4096, 4096, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 N tiles
