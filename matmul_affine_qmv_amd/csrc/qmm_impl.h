@@ -1,5 +1,6 @@
-// qmm_impl.h -- the staged affine quantized x * W^T kernel for M >= 8 on the
-// gfx950 matrix cores.  Included once per code width by qmm_b{2,4,8}.hip.
+// qmm_impl.h -- the staged affine quantized x * W^T kernel on the gfx950
+// matrix cores (M >= 8, and M = 2..7 for large weights).  Included once per
+// code width by qmm_b{1,2,3,4,5,6,8}.hip.
 //
 // Method (page "mlx PR 4682"): transposed affine qmm in which the next K
 // steps' packed weights, scales/biases and activations are fetched while the
@@ -25,9 +26,11 @@
 // * Codes are expanded in registers right before the MFMA into exact 16-bit
 //   integers in natural k order: fields are split into bytes, interleaved,
 //   and one v_perm per pair of codes sets a magic exponent byte above each
-//   (0x43qq is the bf16 value 128 + q, 0x64qq the f16 value 1024 + q).  f16
-//   pairs then drop the 1024 with one exact packed f16 subtraction; for bf16
-//   the constant offset 128*sum(x) is removed in the group epilogue.
+//   (0x43qq is the bf16 value 128 + q, 0x64qq the f16 value 1024 + q).  For
+//   1, 3, 5 and 6 bits a lane's 8 codes are a byte-aligned field of BITS
+//   bytes, cut pair by pair from a two-word window.  f16 pairs then drop the
+//   1024 with one exact packed f16 subtraction; for bf16 the constant offset
+//   128*sum(x) is removed in the group epilogue.
 // * MFMA v_mfma_f32_16x16x32_{bf16,f16}: A = x fragment (16 rows of M),
 //   B = W codes (16 columns of N).  A group of GS codes is GS/32 k-steps
 //   accumulated into a fresh float32 tile; the same A fragments against an
@@ -37,6 +40,9 @@
 //   only roundings are float32 accumulation and the final store.
 // * Work-groups are numbered so that the ones sharing a K range (and so the
 //   same x slice) are dispatched to the same XCD and share its L2.
+// * A batch of problems of one shape is the second grid dimension: each
+//   work-group offsets its operand pointers by its problem's strides (or by
+//   the matrices an index array picks) before anything else.
 #pragma once
 
 #include "qmx_device.h"

@@ -9,9 +9,10 @@
 // gfx950 mapping:
 // * A row group is QMV_ROWS consecutive rows of W, served with up to MT rows
 //   of x.  A wave owns RG row groups (64/RG lanes each) and a contiguous range
-//   of their 16-byte chunks; lane l of a row group takes chunks l, l + 64/RG,
-//   ... of that range, so each load instruction reads 256 B-1 KB contiguous
-//   per row.  KSPLIT waves of one work-group may split the chunks of the same
+//   of their chunks (16 bytes for 2-, 4- and 8-bit codes, BITS words = 32
+//   codes for 1, 3, 5 and 6 bits); lane l of a row group takes chunks l,
+//   l + 64/RG, ... of that range, so each load instruction reads 256 B-1.5 KB
+//   contiguous per row.  KSPLIT waves of one work-group may split the chunks of the same
 //   rows; their partial sums are added in LDS in a fixed order.  The split
 //   (KSPLIT, RG) comes from qmv_split_for.
 // * Loads are buffer loads through resources based at the work-group's first
@@ -25,6 +26,11 @@
 //   removed by using bias - 128*scale in the group epilogue.  x is paired in
 //   the same element order with v_perm.  float32 x (and 8-bit codes with
 //   bf16 x) use per-code conversion and float32 FMA.
+// * 1, 3, 5 and 6 bits: codes 2k and 2k+1 of a chunk are cut as one window
+//   and moved under the magic bytes with a shift-or and an and-or (the magic
+//   held in a register), pairing with x dword k as loaded.
+// * A batch of problems is the third grid dimension (pointers offset by the
+//   problem's strides or index-picked matrices at the start).
 // * The final reductions are fixed xor-butterflies, so results do not change
 //   from run to run.
 #include <algorithm>
