@@ -449,8 +449,36 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             }
         }
         const int c0 = kchunk<BITS, GS>(2 * wk, lgrp), c1 = kchunk<BITS, GS>(2 * wk + 1, lgrp);
-        // one 16-row fragment of x at a time keeps one row of group tiles live; the
-        // group's row sums of x come from one more MFMA against ones
+        if constexpr (NG == 1) {
+            // One group per block and wave: every MFMA of the block first (the group
+            // tiles, and the row sums of x as one more MFMA against ones), then the
+            // float32 epilogue, so the two waves that share a SIMD spend less of the
+            // block issuing the same kind of work at once (measured 1-2% faster).
+            f32x4 gacc[MT][NB], gxs[MT];
+#pragma unroll
+            for (int mf = 0; mf < MT; ++mf) {
+                const int r = mf * 16 + lrow;
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c0 ^ (r & 15)) << 4));
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c1 ^ (r & 15)) << 4));
+#pragma unroll
+                for (int nf = 0; nf < NB; ++nf) {
+                    gacc[mf][nf] = mfma16x16x32<DT>(a0, bf[0][nf], f32x4{0.f, 0.f, 0.f, 0.f});
+                    gacc[mf][nf] = mfma16x16x32<DT>(a1, bf[1][nf], gacc[mf][nf]);
+                }
+                gxs[mf] = mfma16x16x32<DT>(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
+                gxs[mf] = mfma16x16x32<DT>(a1, ones, gxs[mf]);
+            }
+#pragma unroll
+            for (int mf = 0; mf < MT; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < NB; ++nf)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        run[mf][nf][v] = fmaf(sv[0][nf], gacc[mf][nf][v], fmaf(bv[0][nf], gxs[mf][v], run[mf][nf][v]));
+            return;
+        }
+        // two groups per block and wave (GS = 32): one 16-row fragment of x at a
+        // time keeps one row of group tiles live
 #pragma unroll
         for (int mf = 0; mf < MT; ++mf) {
             const int r = mf * 16 + lrow;
@@ -460,21 +488,9 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             for (int gp = 0; gp < NG; ++gp) {
                 f32x4 gacc[NB];
 #pragma unroll
-                for (int nf = 0; nf < NB; ++nf) {
-                    if constexpr (NG == 1) {
-                        gacc[nf] = mfma16x16x32<DT>(a0, bf[0][nf], f32x4{0.f, 0.f, 0.f, 0.f});
-                        gacc[nf] = mfma16x16x32<DT>(a1, bf[1][nf], gacc[nf]);
-                    } else {
-                        gacc[nf] = mfma16x16x32<DT>(gp ? a1 : a0, bf[gp][nf], f32x4{0.f, 0.f, 0.f, 0.f});
-                    }
-                }
-                f32x4 gxs;
-                if constexpr (NG == 1) {
-                    gxs = mfma16x16x32<DT>(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-                    gxs = mfma16x16x32<DT>(a1, ones, gxs);
-                } else {
-                    gxs = mfma16x16x32<DT>(gp ? a1 : a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
-                }
+                for (int nf = 0; nf < NB; ++nf)
+                    gacc[nf] = mfma16x16x32<DT>(gp ? a1 : a0, bf[gp][nf], f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 gxs = mfma16x16x32<DT>(gp ? a1 : a0, ones, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int nf = 0; nf < NB; ++nf)
 #pragma unroll
