@@ -141,6 +141,98 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     return QMX_OK;
 }
 
+// ---------------------------------------------------------------- batched
+// Workspace layout of a batched call: the split-K partials (rounded up to 256
+// bytes), then, when x must be copied, the contiguous copy of x.
+size_t batched_partials_bytes(int batch, int M, int N, int route, int splits) {
+    if (route != QMX_ROUTE_QMM_T_SPLITK) return 0;
+    return ((size_t)splits * batch * M * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+bool x_needs_copy(const void* x, long long xs, long long xr, int dtype) {
+    const long long e = (long long)elem_bytes(dtype);
+    return !is_aligned(x, 16) || (xs * e) % 16 != 0 || (xr * e) % 16 != 0;
+}
+
+int check_batched(int batch, int M, int N, int K, long long ws_, long long sbs, long long xs, long long xr,
+                  int bits, int gs, int dtype) {
+    int rc = check_affine_common(M, N, K, bits, gs, dtype);
+    if (rc) return rc;
+    if (batch < 0 || batch > 65535 || ws_ < 0 || sbs < 0 || xs < 0 || xr < K) return QMX_ERR_SHAPE;
+    // per-problem lane offsets of the vector-ALU route stay in 32 bits
+    if (xr > ((1LL << 31) - 1) / 8 / (long long)elem_bytes(dtype)) return QMX_ERR_SHAPE;
+    if (ws_ % 4 != 0) return QMX_ERR_ALIGN;   // every weight matrix starts 16-byte aligned
+    return QMX_OK;
+}
+
+size_t batched_workspace(int batch, int num_x, int M, int N, int K, int bits, int gs, int dtype, const void* x,
+                         long long xs, long long xr) {
+    int route = 0, splits = 1;
+    if (check_batched(batch, M, N, K, 0, 0, xs, xr, bits, gs, dtype) != QMX_OK) return 0;
+    if (batch == 0 || M == 0 || N == 0) return 0;
+    if (plan_impl(M, N, K, bits, gs, dtype, device_cus(), &route, &splits, batch) != QMX_OK) return 0;
+    size_t bytes = batched_partials_bytes(batch, M, N, route, splits);
+    if (K > 0 && x_needs_copy(x, xs, xr, dtype)) bytes += (size_t)num_x * M * K * elem_bytes(dtype);
+    return bytes;
+}
+
+// Shared body of the batched and gathered calls: w_index/x_index NULL means
+// problem i uses matrix i (num_w = num_x = batch).
+int batched_impl(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
+                 const int* w_index, const int* x_index, int num_w, int num_x, int batch, int M, int N, int K,
+                 long long w_batch_stride, long long sb_batch_stride, long long x_batch_stride,
+                 long long x_row_stride, int bits, int group_size, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int rc = check_batched(batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, bits,
+                           group_size, dtype);
+    if (rc) return rc;
+    if (num_w < 0 || num_x < 0) return QMX_ERR_SHAPE;
+    if (batch == 0 || M == 0 || N == 0) return QMX_OK;
+    if (num_w == 0 || num_x == 0) return QMX_ERR_SHAPE;
+    const int cus = device_cus();
+    if (cus <= 0) return QMX_ERR_DEVICE;
+    int route = 0, splits = 1;
+    rc = plan_impl(M, N, K, bits, group_size, dtype, cus, &route, &splits, batch);
+    if (rc) return rc;
+    if (route == QMX_ROUTE_QMV) {
+        if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
+        if ((long long)((M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M)) > 65535) return QMX_ERR_SHAPE;
+    } else {
+        const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
+        if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
+    }
+    const bool copy_x = K > 0 && x_needs_copy(x, x_batch_stride, x_row_stride, dtype);
+    // pointer checks: x may be at any element offset when it is copied first
+    rc = check_affine_ptrs(w_packed, scales, biases, x, out, K, dtype, 16, copy_x ? elem_bytes(dtype) : 16);
+    if (rc) return rc;
+    if ((w_index && !is_aligned(w_index, 4)) || (x_index && !is_aligned(x_index, 4))) return QMX_ERR_ALIGN;
+    const size_t part_bytes = batched_partials_bytes(batch, M, N, route, splits);
+    const size_t need = part_bytes + (copy_x ? (size_t)num_x * M * K * elem_bytes(dtype) : 0);
+    if (need > 0 && (!workspace || !is_aligned(workspace, 256) || workspace_bytes < need)) return QMX_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    qmx::QmxStrides sd{w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, w_index, x_index, num_w, num_x};
+    if (copy_x) {
+        void* xc = static_cast<unsigned char*>(workspace) + part_bytes;
+        rc = launch_status(qmx::launch_copy_rows(x, xc, num_x, x_batch_stride, x_row_stride, M, K,
+                                                 (int)elem_bytes(dtype), st));
+        if (rc) return rc;
+        x = xc;
+        sd.x = (long long)M * K;
+        sd.x_row = K;
+    }
+    if (route == QMX_ROUTE_QMV)
+        return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, batch, sd, M, N, K, bits, group_size,
+                                             dtype, st));
+    if (route == QMX_ROUTE_QMM_T)
+        return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, batch, sd, M, N, K, bits,
+                                               group_size, dtype, 1, st));
+    float* ws = static_cast<float*>(workspace);
+    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, batch, sd, M, N, K, bits, group_size,
+                                         dtype, splits, st));
+    if (rc) return rc;
+    return launch_status(qmx::launch_splitk_accum(ws, out, splits, (size_t)batch * M * N, dtype, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,112 +388,12 @@ int qmx_qmm(const uint32_t* w_packed, const void* scales, const void* biases, co
                             workspace, workspace_bytes, stream);
 }
 
-// ---------------------------------------------------------------- batched
-// Workspace layout of a batched call: the split-K partials (rounded up to 256
-// bytes), then, when x must be copied, the contiguous copy of x.
-static size_t batched_partials_bytes(int batch, int M, int N, int route, int splits) {
-    if (route != QMX_ROUTE_QMM_T_SPLITK) return 0;
-    return ((size_t)splits * batch * M * N * sizeof(float) + 255) & ~(size_t)255;
-}
-
-static bool x_needs_copy(const void* x, long long xs, long long xr, int dtype) {
-    const long long e = (long long)elem_bytes(dtype);
-    return !is_aligned(x, 16) || (xs * e) % 16 != 0 || (xr * e) % 16 != 0;
-}
-
-static int check_batched(int batch, int M, int N, int K, long long ws_, long long sbs, long long xs, long long xr,
-                         int bits, int gs, int dtype) {
-    int rc = check_affine_common(M, N, K, bits, gs, dtype);
-    if (rc) return rc;
-    if (batch < 0 || batch > 65535 || ws_ < 0 || sbs < 0 || xs < 0 || xr < K) return QMX_ERR_SHAPE;
-    // per-problem lane offsets of the vector-ALU route stay in 32 bits
-    if (xr > ((1LL << 31) - 1) / 8 / (long long)elem_bytes(dtype)) return QMX_ERR_SHAPE;
-    if (ws_ % 4 != 0) return QMX_ERR_ALIGN;   // every weight matrix starts 16-byte aligned
-    return QMX_OK;
-}
-
 int qmx_plan_batched(int batch, int M, int N, int K, int bits, int group_size, int dtype, int num_cus, int* route,
                      int* splits) {
     if (!route || !splits) return QMX_ERR_NULL;
     if (batch < 0 || batch > 65535) return QMX_ERR_SHAPE;
     return plan_impl(M, N, K, bits, group_size, dtype, num_cus, route, splits, batch > 0 ? batch : 1);
 }
-
-}  // extern "C"
-
-namespace {
-
-size_t batched_workspace(int batch, int num_x, int M, int N, int K, int bits, int gs, int dtype, const void* x,
-                         long long xs, long long xr) {
-    int route = 0, splits = 1;
-    if (check_batched(batch, M, N, K, 0, 0, xs, xr, bits, gs, dtype) != QMX_OK) return 0;
-    if (batch == 0 || M == 0 || N == 0) return 0;
-    if (plan_impl(M, N, K, bits, gs, dtype, device_cus(), &route, &splits, batch) != QMX_OK) return 0;
-    size_t bytes = batched_partials_bytes(batch, M, N, route, splits);
-    if (K > 0 && x_needs_copy(x, xs, xr, dtype)) bytes += (size_t)num_x * M * K * elem_bytes(dtype);
-    return bytes;
-}
-
-// Shared body of the batched and gathered calls: w_index/x_index NULL means
-// problem i uses matrix i (num_w = num_x = batch).
-int batched_impl(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
-                 const int* w_index, const int* x_index, int num_w, int num_x, int batch, int M, int N, int K,
-                 long long w_batch_stride, long long sb_batch_stride, long long x_batch_stride,
-                 long long x_row_stride, int bits, int group_size, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-    int rc = check_batched(batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, bits,
-                           group_size, dtype);
-    if (rc) return rc;
-    if (num_w < 0 || num_x < 0) return QMX_ERR_SHAPE;
-    if (batch == 0 || M == 0 || N == 0) return QMX_OK;
-    if (num_w == 0 || num_x == 0) return QMX_ERR_SHAPE;
-    const int cus = device_cus();
-    if (cus <= 0) return QMX_ERR_DEVICE;
-    int route = 0, splits = 1;
-    rc = plan_impl(M, N, K, bits, group_size, dtype, cus, &route, &splits, batch);
-    if (rc) return rc;
-    if (route == QMX_ROUTE_QMV) {
-        if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
-        if ((long long)((M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M)) > 65535) return QMX_ERR_SHAPE;
-    } else {
-        const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
-        if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
-    }
-    const bool copy_x = K > 0 && x_needs_copy(x, x_batch_stride, x_row_stride, dtype);
-    // pointer checks: x may be at any element offset when it is copied first
-    rc = check_affine_ptrs(w_packed, scales, biases, x, out, K, dtype, 16, copy_x ? elem_bytes(dtype) : 16);
-    if (rc) return rc;
-    if ((w_index && !is_aligned(w_index, 4)) || (x_index && !is_aligned(x_index, 4))) return QMX_ERR_ALIGN;
-    const size_t part_bytes = batched_partials_bytes(batch, M, N, route, splits);
-    const size_t need = part_bytes + (copy_x ? (size_t)num_x * M * K * elem_bytes(dtype) : 0);
-    if (need > 0 && (!workspace || !is_aligned(workspace, 256) || workspace_bytes < need)) return QMX_ERR_WORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    qmx::QmxStrides sd{w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, w_index, x_index, num_w, num_x};
-    if (copy_x) {
-        void* xc = static_cast<unsigned char*>(workspace) + part_bytes;
-        rc = launch_status(qmx::launch_copy_rows(x, xc, num_x, x_batch_stride, x_row_stride, M, K,
-                                                 (int)elem_bytes(dtype), st));
-        if (rc) return rc;
-        x = xc;
-        sd.x = (long long)M * K;
-        sd.x_row = K;
-    }
-    if (route == QMX_ROUTE_QMV)
-        return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, batch, sd, M, N, K, bits, group_size,
-                                             dtype, st));
-    if (route == QMX_ROUTE_QMM_T)
-        return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, batch, sd, M, N, K, bits,
-                                               group_size, dtype, 1, st));
-    float* ws = static_cast<float*>(workspace);
-    rc = launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, ws, batch, sd, M, N, K, bits, group_size,
-                                         dtype, splits, st));
-    if (rc) return rc;
-    return launch_status(qmx::launch_splitk_accum(ws, out, splits, (size_t)batch * M * N, dtype, st));
-}
-
-}  // namespace
-
-extern "C" {
 
 size_t qmx_qmm_batched_workspace_bytes(int batch, int M, int N, int K, int bits, int group_size, int dtype,
                                        const void* x, long long x_batch_stride, long long x_row_stride) {
