@@ -45,9 +45,12 @@ F32, F16, BF16 = 0, 1, 2
 DT_NAME = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 
-def affine(route, M, N, K, dt=BF16, bits=4, gs=64, B=1, E=1):
-    return {"kind": "affine", "route": route, "M": M, "N": N, "K": K, "bits": bits, "gs": gs, "dtype": dt, "B": B,
-            "E": E}
+def affine(route, M, N, K, dt=BF16, bits=4, gs=64, B=1, E=1, sorted_idx=False):
+    c = {"kind": "affine", "route": route, "M": M, "N": N, "K": K, "bits": bits, "gs": gs, "dtype": dt, "B": B,
+         "E": E}
+    if sorted_idx:   # gather with the problems ordered by weight matrix (qmx_qmm_gather_sorted)
+        c["sorted"] = True
+    return c
 
 
 def block(kind, N, K):
@@ -80,8 +83,10 @@ WORKLOADS = {
     "batched_4bit_gs64_bf16": [affine("batched", 1, 4096, 4096, B=8), affine("batched", 16, 2048, 4096, B=8),
                                affine("batched", 56, 2048, 5120, B=4)],
     # B problems gathering from E weight matrices (qmx_qmm_gather; every matrix is used, each by
-    # B/E problems), illustrative shapes as above
-    "gather_4bit_gs64_bf16": [affine("gather", 1, 2048, 4096, B=16, E=8), affine("gather", 16, 2048, 4096, B=16, E=8)],
+    # B/E problems, in random order; then the same picks ordered by matrix through
+    # qmx_qmm_gather_sorted), illustrative shapes as above
+    "gather_4bit_gs64_bf16": [affine("gather", 1, 2048, 4096, B=16, E=8), affine("gather", 16, 2048, 4096, B=16, E=8),
+                              affine("gather", 1, 2048, 4096, B=16, E=8, sorted_idx=True)],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
     "q8_i8_14336x5120": [block("q8_i8", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
@@ -93,7 +98,7 @@ def call_name(c):
     if c["kind"] == "affine":
         head = c["route"] if c.get("B", 1) == 1 else f"{c['route']}{c['B']}"
         if c["route"] == "gather":
-            head += f"of{c['E']}"
+            head = head.replace("gather", "gathersorted" if c.get("sorted") else "gather") + f"of{c['E']}"
         return f"{head}_M{c['M']}_N{c['N']}_K{c['K']}_b{c['bits']}_gs{c['gs']}_{DT_NAME[c['dtype']]}"
     return f"{c['kind']}_N{c['N']}_K{c['K']}"
 
@@ -160,7 +165,10 @@ def make_inputs(c, seed, dev):
                                                    dev)["x"] for i in range(c["B"])])
         g = torch.Generator(device="cpu")
         g.manual_seed(seed)
-        d["w_index"] = (torch.randperm(c["B"], generator=g) % c["E"]).to(torch.int32).to(dev)
+        wi = torch.randperm(c["B"], generator=g) % c["E"]
+        if c.get("sorted"):
+            wi = torch.sort(wi).values
+        d["w_index"] = wi.to(torch.int32).to(dev)
         d["out"] = torch.empty((c["B"], c["M"], c["N"]), dtype=d["x"].dtype, device=dev)
         need = qmx.lib().qmx_qmm_gather_workspace_bytes(c["B"], c["B"], c["M"], c["N"], c["K"], c["bits"], c["gs"],
                                                          c["dtype"], d["x"].data_ptr(), c["M"] * c["K"], c["K"])
@@ -209,7 +217,7 @@ def launch(c, d):
     kw = dict(bits=c["bits"], group_size=c["gs"])
     if c["route"] == "gather":
         return qmx.gather_qmm(d["w"], d["scales"], d["biases"], d["x"], d["w_index"], None, d["out"],
-                              workspace=d["ws"], **kw)
+                              workspace=d["ws"], sorted_indices=c.get("sorted", False), **kw)
     if c["route"] == "batched":
         return qmx.qmm_batched(d["w"], d["scales"], d["biases"], d["x"], d["out"], workspace=d["ws"], **kw)
     if c["route"] == "qmv":

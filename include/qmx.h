@@ -297,6 +297,30 @@ size_t qmx_qmm_gather_workspace_bytes(int batch, int num_x, int M, int N, int K,
                                       int group_size, int dtype, const void* x,
                                       long long x_batch_stride, long long x_row_stride);
 
+/* qmx_qmm_gather_sorted -- qmx_qmm_gather for a w_index that holds runs of
+ * equal values, as a mixture-of-experts router's output does once the
+ * problems are ordered by expert (the gathered qmm of page "mlx PR 4682";
+ * the grouping below is this library's).  Arguments, workspace
+ * (qmx_qmm_gather_workspace_bytes), results within the same tolerance, and
+ * errors as qmx_qmm_gather, for any index arrays: sortedness only decides
+ * how much work is shared, never what is computed.
+ * At M = 1 on the vector route, one work-group serves up to g consecutive
+ * problems whose clamped w_index values are equal, as the x rows of one tile,
+ * so a run of problems on one weight matrix streams those weights once
+ * rather than once per problem.  g = 1, 2 or 4 is the run length that
+ * batch / num_w suggests (rounded up; 4 from 3 on).  Runs are cut at
+ * multiples of g.  Other shapes, and x matrices spanning 2 GiB or more, run
+ * as qmx_qmm_gather.  Reruns with the same inputs are bit-identical; the
+ * float32 summation order can differ from qmx_qmm_gather's.
+ */
+int qmx_qmm_gather_sorted(const uint32_t* w_packed, const void* scales, const void* biases,
+                          const void* x, void* out, const int32_t* w_index,
+                          const int32_t* x_index, int num_w, int num_x, int batch, int M, int N,
+                          int K, long long w_batch_stride, long long sb_batch_stride,
+                          long long x_batch_stride, long long x_row_stride, int bits,
+                          int group_size, int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* qmx_plan for a batch: the tiles of all problems share the device, so a
  * batch needs fewer K partitions.  Pure host function. */
 int qmx_plan_batched(int batch, int M, int N, int K, int bits, int group_size, int dtype,

@@ -54,6 +54,8 @@ _EXPORTS = {
     "qmx_plan_batched": (ctypes.c_int, [ctypes.c_int] * 8 + [ctypes.POINTER(ctypes.c_int)] * 2),
     "qmx_qmm_gather": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 6 + [ctypes.c_longlong] * 4
                        + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "qmx_qmm_gather_sorted": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 6 + [ctypes.c_longlong] * 4
+                              + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "qmx_qmm_gather_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 8 + [ctypes.c_void_p]
                                        + [ctypes.c_longlong] * 2),
     "qmx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -323,13 +325,14 @@ def qmm_batched(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64,
 
 
 def gather_qmm(w_packed, scales, biases, x, w_index=None, x_index=None, out=None, *, bits=4, group_size=64,
-               workspace=None):
+               workspace=None, sorted_indices=False):
     """Gathered quantized matmul (qmx_qmm_gather): out[i] = x[x_index[i]] @
     dequant(W[w_index[i]]).T.  w_packed [E, N, K*bits/32] and scales/biases
     [E, N, K/group_size] (each matrix contiguous); x [X, M, K] with a unit last
     stride (any batch/row stride and offset); w_index, x_index: int32 device
     vectors of one length B (None: identity, then that operand has B matrices);
-    out: contiguous [B, M, N]."""
+    out: contiguous [B, M, N].  sorted_indices: w_index holds runs of equal
+    values (qmx_qmm_gather_sorted; the same results for any indices)."""
     if x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("x must be [X, M, K] with a unit last stride")
     if w_packed.dim() != 3 or scales.dim() != 3 or biases.dim() != 3:
@@ -376,10 +379,11 @@ def gather_qmm(w_packed, scales, biases, x, w_index=None, x_index=None, out=None
         workspace = _workspace(x, need, None)
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().qmx_qmm_gather(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), _ptr(w_index),
+    name = "qmx_qmm_gather_sorted" if sorted_indices else "qmx_qmm_gather"
+    _check(getattr(lib(), name)(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), _ptr(w_index),
                                 _ptr(x_index), E, X, B, M, N, K, w_packed.stride(0) if E > 1 else 0,
                                 scales.stride(0) if E > 1 else 0, xs, xr, bits, group_size, dt, ws_ptr, ws_bytes,
-                                _stream(x)), "qmx_qmm_gather")
+                                _stream(x)), name)
     return out
 
 

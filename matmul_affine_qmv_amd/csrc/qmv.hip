@@ -30,7 +30,9 @@
 //   and moved under the magic bytes with a shift-or and an and-or (the magic
 //   held in a register), pairing with x dword k as loaded.
 // * A batch of problems is the third grid dimension (pointers offset by the
-//   problem's strides or index-picked matrices at the start).
+//   problem's strides or index-picked matrices at the start).  A gather at
+//   M = 1 may group consecutive problems on one weight matrix into the x rows
+//   of one tile, so that matrix streams once for all of them.
 // * The final reductions are fixed xor-butterflies, so results do not change
 //   from run to run.
 #include <algorithm>
@@ -433,13 +435,27 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     constexpr int LP = 64 / RG;   // lanes per row group
     using S = QmvStage<DT, BITS, GS, MT>;
     // problem blockIdx.z of the batch
+    const long long bz = blockIdx.z;
+    // Grouped gather (M = 1): problem bz leads a tile when it sits at a multiple
+    // of the group size or picks another weight matrix than problem bz - 1; its
+    // tile then takes the following problems up to the next such leader, as x
+    // rows 1, 2, ... (their outputs are the rows that follow in `out`).  Every
+    // other problem belongs to a leader's tile and its work-group exits.
+    int gcount = 1;
     {
         constexpr int E = DT == DT_F32 ? 4 : 2;
-        const long long bz = blockIdx.z, wz = qmx_w_matrix(sd, bz), xz = qmx_x_matrix(sd, bz);
+        const long long wz = qmx_w_matrix(sd, bz);
+        if (sd.group > 1) {
+            if (bz % sd.group != 0 && qmx_w_matrix(sd, bz - 1) == wz) return;
+            while (gcount < sd.group && bz + gcount < (long long)gridDim.z && (bz + gcount) % sd.group != 0 &&
+                   qmx_w_matrix(sd, bz + gcount) == wz)
+                ++gcount;
+        } else {
+            x = static_cast<const unsigned char*>(x) + qmx_x_matrix(sd, bz) * sd.x * E;
+        }
         w += wz * sd.w;
         scales = static_cast<const unsigned char*>(scales) + wz * sd.sb * E;
         biases = static_cast<const unsigned char*>(biases) + wz * sd.sb * E;
-        x = static_cast<const unsigned char*>(x) + xz * sd.x * E;
         out = static_cast<unsigned char*>(out) + bz * M * (long long)N * E;
     }
     const int XR = (int)sd.x_row;
@@ -448,7 +464,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     const int nw = blockIdx.x * RG * R;          // first row of the work-group
     const int n0 = nw + lp * R;                   // first row of this lane's row group
     const int m0 = blockIdx.y * MT;
-    const int mcount = min(MT, M - m0);
+    const int mcount = sd.group > 1 ? gcount : min(MT, M - m0);
     const int G = K / GS;
     const int chunks = K / S::CPC;
     const size_t row_bytes = (size_t)K * BITS / 8;
@@ -462,16 +478,28 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     ad.w = buffer_over(reinterpret_cast<const unsigned char*>(w) + (size_t)nw * row_bytes, (size_t)(N - nw) * row_bytes);
     ad.s = buffer_over(static_cast<const unsigned char*>(scales) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
     ad.b = buffer_over(static_cast<const unsigned char*>(biases) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
-    ad.x = buffer_over(static_cast<const unsigned char*>(x) + (size_t)m0 * XR * EB,
-                       ((size_t)(M - m0 - 1) * XR + K) * EB);
+    if (sd.group > 1) {
+        // x rows of the tile's problems, addressed from the first x matrix
+        const long long nx = sd.x_index ? sd.num_x : (long long)gridDim.z;
+        ad.x = buffer_over(x, (size_t)((nx - 1) * sd.x + K) * EB);
+    } else {
+        ad.x = buffer_over(static_cast<const unsigned char*>(x) + (size_t)m0 * XR * EB,
+                           ((size_t)(M - m0 - 1) * XR + K) * EB);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int rr = min(n0 + r, N - 1) - nw;
         ad.vw[r] = (int)((size_t)rr * row_bytes) + 4 * S::CW * c;
         ad.vsb[r] = (rr * G + (c * S::CPC) / GS) * EB;
     }
+    if (sd.group > 1) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * XR + c * S::CPC) * EB;
+        for (int m = 0; m < MT; ++m)
+            ad.vx[m] = (int)((qmx_x_matrix(sd, bz + (m < mcount ? m : 0)) * sd.x + c * S::CPC) * EB);
+    } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) ad.vx[m] = ((m < mcount ? m : 0) * XR + c * S::CPC) * EB;
+    }
     // per-round scalar steps
     constexpr int STEP_W = LP * 4 * S::CW, STEP_SB = LP * S::CPC / GS * EB, STEP_X = LP * S::CPC * EB;
     static_assert((LP * S::CPC) % GS == 0, "a round advances by whole groups");
@@ -580,7 +608,7 @@ static void qmv_go(int batch, QmxStrides sd, int M, int N, int K, const uint32_t
 template <int DT, int BITS, int GS>
 static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
                          QmxStrides sd, int M, int N, int K, hipStream_t st) {
-    const int mt = qmv_mt_for(M);
+    const int mt = qmv_mt_for(sd.group > 1 ? sd.group : M);
 #define QMV_GO(MT_, KS_, RG_) qmv_go<DT, BITS, GS, MT_, KS_, RG_>(batch, sd, M, N, K, w, s, b, x, out, st)
     if (mt == 1) {
         const QmvSplit sp = qmv_split_for(M, (long long)N * batch, K, BITS);
@@ -629,6 +657,7 @@ static hipError_t qmv_bits(const uint32_t* w, const void* s, const void* b, cons
 hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                       int batch, QmxStrides sd, int M, int N, int K, int bits, int gs, int dt,
                       hipStream_t st) {
+    if (M != 1 || !sd.w_index) sd.group = 1;   // grouping is defined for single-row gathers only
     switch (dt) {
         case DT_F32: return qmv_bits<DT_F32>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
         case DT_F16: return qmv_bits<DT_F16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);

@@ -176,13 +176,22 @@ size_t batched_workspace(int batch, int num_x, int M, int N, int K, int bits, in
     return bytes;
 }
 
+// Problems per vector-route tile for a gather whose w_index holds runs of
+// equal values: the run length a balanced sorted index gives (batch / num_w,
+// rounded up), as 1, 2 or 4.
+int gather_group(int batch, int num_w) {
+    const int run = (batch + num_w - 1) / num_w;
+    return run >= 3 ? 4 : run == 2 ? 2 : 1;
+}
+
 // Shared body of the batched and gathered calls: w_index/x_index NULL means
-// problem i uses matrix i (num_w = num_x = batch).
+// problem i uses matrix i (num_w = num_x = batch).  `sorted`: w_index is
+// expected to hold runs of equal values (see gather_group).
 int batched_impl(const uint32_t* w_packed, const void* scales, const void* biases, const void* x, void* out,
                  const int* w_index, const int* x_index, int num_w, int num_x, int batch, int M, int N, int K,
                  long long w_batch_stride, long long sb_batch_stride, long long x_batch_stride,
                  long long x_row_stride, int bits, int group_size, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, void* stream, bool sorted = false) {
     int rc = check_batched(batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride, x_row_stride, bits,
                            group_size, dtype);
     if (rc) return rc;
@@ -219,6 +228,11 @@ int batched_impl(const uint32_t* w_packed, const void* scales, const void* biase
         x = xc;
         sd.x = (long long)M * K;
         sd.x_row = K;
+    }
+    if (sorted && w_index && route == QMX_ROUTE_QMV && M == 1) {
+        // a grouped tile addresses its x rows from the first x matrix in 32 bits
+        const int g = gather_group(batch, num_w);
+        if (g > 1 && ((long long)(num_x - 1) * sd.x + K) * (long long)elem_bytes(dtype) < (1LL << 31)) sd.group = g;
     }
     if (route == QMX_ROUTE_QMV)
         return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, batch, sd, M, N, K, bits, group_size,
@@ -423,6 +437,16 @@ int qmx_qmm_gather(const uint32_t* w_packed, const void* scales, const void* bia
     return batched_impl(w_packed, scales, biases, x, out, w_index, x_index, w_index ? num_w : batch,
                         x_index ? num_x : batch, batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride,
                         x_row_stride, bits, group_size, dtype, workspace, workspace_bytes, stream);
+}
+
+int qmx_qmm_gather_sorted(const uint32_t* w_packed, const void* scales, const void* biases, const void* x,
+                          void* out, const int32_t* w_index, const int32_t* x_index, int num_w, int num_x,
+                          int batch, int M, int N, int K, long long w_batch_stride, long long sb_batch_stride,
+                          long long x_batch_stride, long long x_row_stride, int bits, int group_size, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return batched_impl(w_packed, scales, biases, x, out, w_index, x_index, w_index ? num_w : batch,
+                        x_index ? num_x : batch, batch, M, N, K, w_batch_stride, sb_batch_stride, x_batch_stride,
+                        x_row_stride, bits, group_size, dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -249,13 +249,15 @@ def test_batched_plan_counts_every_problem():
 def test_gather_validation():
     L = qmx.lib()
 
-    def gat(B=3, nw=2, nx=2, M=4, N=64, K=512, w=FAKE, x=FAKE, o=FAKE, wi=FAKE, xi=FAKE):
-        return L.qmx_qmm_gather(w, FAKE, FAKE, x, o, wi, xi, nw, nx, B, M, N, K, 128, 64, 2048, 512, 4, 64, BF16,
-                                None, 0, None)
+    for fn in (L.qmx_qmm_gather, L.qmx_qmm_gather_sorted):
+        def gat(B=3, nw=2, nx=2, M=4, N=64, K=512, w=FAKE, x=FAKE, o=FAKE, wi=FAKE, xi=FAKE):
+            return fn(w, FAKE, FAKE, x, o, wi, xi, nw, nx, B, M, N, K, 128, 64, 2048, 512, 4, 64, BF16,
+                      None, 0, None)
 
-    assert gat(nw=0) == ESHAPE                # a non-empty batch needs at least one weight matrix
-    assert gat(nx=-1) == ESHAPE
-    assert gat(B=0, w=None, x=None, o=None, wi=None, xi=None) == OK
+        assert gat(nw=0) == ESHAPE                # a non-empty batch needs at least one weight matrix
+        assert gat(nx=-1) == ESHAPE
+        assert gat(M=1, nw=0) == ESHAPE
+        assert gat(B=0, w=None, x=None, o=None, wi=None, xi=None) == OK
     assert L.qmx_qmm_gather_workspace_bytes(3, 2, 4, 64, 512, 4, 64, BF16, ODD, 2048, 512) == 2 * 4 * 512 * 2
 
 

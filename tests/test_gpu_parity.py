@@ -510,6 +510,69 @@ def test_gather_qmm(orc, M, N, K, bits, gs, dt, layout):
     assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
 
 
+@pytest.mark.parametrize("N,K,bits,gs,dt,w_index,x_index,layout", [
+    # B/E = 12/5: tiles of up to 4 problems; a run of 5 is cut at problem 4
+    (200, 1024, 4, 64, qi.BF16, [0, 0, 0, 0, 0, 1, 2, 2, 3, 3, 3, 4], None, "contiguous"),
+    # B/E = 2: tiles of up to 2; x picked out of order
+    (192, 2048, 4, 64, qi.F16, [0, 0, 1, 1, 1, 2, 3, 3], [3, 0, 2, 1, 3, 0, 1, 2], "contiguous"),
+    (96, 512, 8, 32, qi.F32, [0, 0, 0, 1, 1, 1, 1, 2, 2], None, "contiguous"),
+    (130, 768, 3, 128, qi.BF16, [1, 1, 1, 0, 0, 2, 2, 2], None, "odd"),     # x copied first
+    (64, 1024, 6, 64, qi.F16, [4, 4, 4, 4, 4, 4, 4, 4], [0, 1, 0, 1, 0, 1, 0, 1], "padded"),
+    # not sorted: the same results, fewer problems share a tile
+    (160, 1024, 4, 64, qi.BF16, [2, 0, 2, 2, 1, 0, 0, 2, 1, 1], None, "contiguous"),
+    # out-of-range picks clamp first: -3, 0 -> 0 and 99, 4 -> 4 form runs
+    (64, 512, 2, 32, qi.BF16, [-3, 0, 0, 2, 99, 4, 4, 4], None, "contiguous"),
+])
+def test_gather_sorted_groups(orc, N, K, bits, gs, dt, w_index, x_index, layout):
+    """qmx_qmm_gather_sorted at M = 1: consecutive problems on one weight
+    matrix share a tile; every output matches the oracle of its (W, x) pair,
+    and reruns are bit-identical."""
+    E = 5
+    B = len(w_index)
+    X = 4 if x_index is not None else B
+    say("gather_sorted", N, K, bits, gs, qi.DTYPE_NAMES[dt], layout, w_index, x_index)
+    wc = [qi.affine_case(1, N, K, bits, gs, dt, seed=2800 + e) for e in range(E)]
+    xc = [qi.affine_case(1, 32, K, 4, gs, dt, seed=2850 + j)["x"] for j in range(X)]
+    parts = [to_dev(c) for c in wc]
+    w, s, b = (torch.stack([p[j] for p in parts]) for j in range(3))
+    x = _strided(torch.stack([qmx.storage_tensor(v, dt, DEV) for v in xc]), layout)
+    wi = torch.tensor(w_index, dtype=torch.int32, device=DEV)
+    xi = torch.tensor(x_index, dtype=torch.int32, device=DEV) if x_index is not None else None
+    y = qmx.gather_qmm(w, s, b, x, wi, xi, bits=bits, group_size=gs, sorted_indices=True)
+    y2 = qmx.gather_qmm(w, s, b, x, wi, xi, bits=bits, group_size=gs, sorted_indices=True)
+    torch.cuda.synchronize()
+    got = out64(y, dt)
+    for i in range(B):
+        we = min(max(w_index[i], 0), E - 1)
+        xe = x_index[i] if x_index is not None else i
+        c = wc[we]
+        ref = orc.affine(c["w"], c["scales"], c["biases"], dt, xc[xe], dt, 1, N, K, bits, gs)
+        assert_close(got[i], ref, dt, orc, what=f"sorted gather problem {i}: W{we} x{xe}")
+    assert torch.equal(y.view(torch.uint8), y2.view(torch.uint8))
+
+
+def test_gather_sorted_other_shapes(orc):
+    """Shapes the grouping does not cover (M > 1) run as the plain gather."""
+    M, N, K, bits, gs, dt = 3, 128, 1024, 4, 64, qi.BF16
+    w_index = [0, 0, 1, 1, 1]
+    say("gather_sorted M=3", N, K, w_index)
+    wc = [qi.affine_case(1, N, K, bits, gs, dt, seed=2900 + e) for e in range(2)]
+    xc = [qi.affine_case(M, 32, K, 4, gs, dt, seed=2950 + j)["x"] for j in range(len(w_index))]
+    parts = [to_dev(c) for c in wc]
+    w, s, b = (torch.stack([p[j] for p in parts]) for j in range(3))
+    x = torch.stack([qmx.storage_tensor(v, dt, DEV) for v in xc])
+    wi = torch.tensor(w_index, dtype=torch.int32, device=DEV)
+    y = qmx.gather_qmm(w, s, b, x, wi, bits=bits, group_size=gs, sorted_indices=True)
+    yp = qmx.gather_qmm(w, s, b, x, wi, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yp.view(torch.int16))
+    got = out64(y, dt)
+    for i, e in enumerate(w_index):
+        c = wc[e]
+        ref = orc.affine(c["w"], c["scales"], c["biases"], dt, xc[i], dt, M, N, K, bits, gs)
+        assert_close(got[i], ref, dt, orc, what=f"sorted gather M=3 problem {i}")
+
+
 # ---------------------------------------------------------------- integer activations
 def _q8_i8_dev(c):
     return (qmx.words_tensor(c["wq"], DEV), qmx.words_tensor(c["xq"], DEV),
