@@ -20,8 +20,8 @@ is not timed.  `value` is algorithmic bytes moved per second over the K timed
 steps (GB/s); per-call microseconds come from HIP events around graphs that
 replay one call over the rotating sets.
 
-One JSON line is printed on stdout.  `--gpus` above 1 is refused: this
-build runs on one GPU.
+One JSON line is printed on stdout.  `--gpus` above 1 is refused: the
+benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -406,7 +406,7 @@ def cpu_baseline(calls, sets, target_s):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on exactly one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark runs on exactly one GPU "
               f"(the hot path would shard across GPUs by output rows of W)", file=sys.stderr)
         return 2
     import torch
