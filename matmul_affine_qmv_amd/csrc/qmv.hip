@@ -424,7 +424,7 @@ __device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st
         }
 }
 
-template <int DT, int BITS, int GS, int MT, int KSPLIT, int RG>
+template <int DT, int BITS, int GS, int MT, int KSPLIT, int RG, int GROUP>
 __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __restrict__ w,
                                                           const void* __restrict__ scales,
                                                           const void* __restrict__ biases,
@@ -436,26 +436,25 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     using S = QmvStage<DT, BITS, GS, MT>;
     // problem blockIdx.z of the batch
     const long long bz = blockIdx.z;
-    // Grouped gather (M = 1): problem bz leads a tile when it sits at a multiple
-    // of the group size or picks another weight matrix than problem bz - 1; its
-    // tile then takes the following problems up to the next such leader, as x
-    // rows 1, 2, ... (their outputs are the rows that follow in `out`).  Every
-    // other problem belongs to a leader's tile and its work-group exits.
+    // Grouped gather (GROUP > 1, M = 1): problem bz leads a tile when it sits at
+    // a multiple of GROUP or picks another weight matrix than problem bz - 1;
+    // its tile then takes the following problems up to the next such leader,
+    // as x rows 1, 2, ... (their outputs are the rows that follow in `out`).
+    // Every other problem belongs to a leader's tile and its work-group exits.
     int gcount = 1;
     {
         constexpr int E = DT == DT_F32 ? 4 : 2;
         const long long wz = qmx_w_matrix(sd, bz);
-        if (sd.group > 1) {
-            if (bz % sd.group != 0 && qmx_w_matrix(sd, bz - 1) == wz) return;
-            while (gcount < sd.group && bz + gcount < (long long)gridDim.z && (bz + gcount) % sd.group != 0 &&
+        if constexpr (GROUP > 1) {
+            if (bz % GROUP != 0 && qmx_w_matrix(sd, bz - 1) == wz) return;
+            while (gcount < GROUP && bz + gcount < (long long)gridDim.z && (bz + gcount) % GROUP != 0 &&
                    qmx_w_matrix(sd, bz + gcount) == wz)
                 ++gcount;
-        } else {
-            x = static_cast<const unsigned char*>(x) + qmx_x_matrix(sd, bz) * sd.x * E;
         }
         w += wz * sd.w;
         scales = static_cast<const unsigned char*>(scales) + wz * sd.sb * E;
         biases = static_cast<const unsigned char*>(biases) + wz * sd.sb * E;
+        if constexpr (GROUP == 1) x = static_cast<const unsigned char*>(x) + qmx_x_matrix(sd, bz) * sd.x * E;
         out = static_cast<unsigned char*>(out) + bz * M * (long long)N * E;
     }
     const int XR = (int)sd.x_row;
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     const int nw = blockIdx.x * RG * R;          // first row of the work-group
     const int n0 = nw + lp * R;                   // first row of this lane's row group
     const int m0 = blockIdx.y * MT;
-    const int mcount = sd.group > 1 ? gcount : min(MT, M - m0);
+    const int mcount = GROUP > 1 ? gcount : min(MT, M - m0);
     const int G = K / GS;
     const int chunks = K / S::CPC;
     const size_t row_bytes = (size_t)K * BITS / 8;
@@ -478,7 +477,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     ad.w = buffer_over(reinterpret_cast<const unsigned char*>(w) + (size_t)nw * row_bytes, (size_t)(N - nw) * row_bytes);
     ad.s = buffer_over(static_cast<const unsigned char*>(scales) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
     ad.b = buffer_over(static_cast<const unsigned char*>(biases) + (size_t)nw * G * EB, (size_t)(N - nw) * G * EB);
-    if (sd.group > 1) {
+    if constexpr (GROUP > 1) {
         // x rows of the tile's problems, addressed from the first x matrix
         const long long nx = sd.x_index ? sd.num_x : (long long)gridDim.z;
         ad.x = buffer_over(x, (size_t)((nx - 1) * sd.x + K) * EB);
@@ -492,7 +491,7 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
         ad.vw[r] = (int)((size_t)rr * row_bytes) + 4 * S::CW * c;
         ad.vsb[r] = (rr * G + (c * S::CPC) / GS) * EB;
     }
-    if (sd.group > 1) {
+    if constexpr (GROUP > 1) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             ad.vx[m] = (int)((qmx_x_matrix(sd, bz + (m < mcount ? m : 0)) * sd.x + c * S::CPC) * EB);
@@ -597,19 +596,28 @@ QmvSplit qmv_split_for(int M, long long N, int K, int bits) {
     return best;
 }
 
-template <int DT, int BITS, int GS, int MT, int KS, int RG>
+template <int DT, int BITS, int GS, int MT, int KS, int RG, int GROUP = 1>
 static void qmv_go(int batch, QmxStrides sd, int M, int N, int K, const uint32_t* w, const void* s, const void* b,
                    const void* x, void* out, hipStream_t st) {
     const dim3 grid((N + QMV_ROWS * RG - 1) / (QMV_ROWS * RG), (M + MT - 1) / MT, batch);
-    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS, RG>), grid, dim3(64 * KS), 0, st, w, s, b, x, out, sd,
-                       M, N, K);
+    hipLaunchKernelGGL((qmv_kernel<DT, BITS, GS, MT, KS, RG, GROUP>), grid, dim3(64 * KS), 0, st, w, s, b, x, out,
+                       sd, M, N, K);
 }
 
 template <int DT, int BITS, int GS>
 static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
-                         QmxStrides sd, int M, int N, int K, hipStream_t st) {
-    const int mt = qmv_mt_for(sd.group > 1 ? sd.group : M);
+                         QmxStrides sd, int M, int N, int K, int group, hipStream_t st) {
 #define QMV_GO(MT_, KS_, RG_) qmv_go<DT, BITS, GS, MT_, KS_, RG_>(batch, sd, M, N, K, w, s, b, x, out, st)
+    // grouped gathers: a tile of `group` x rows, one per problem
+    if (group == 2) {
+        qmv_go<DT, BITS, GS, 2, 1, 1, 2>(batch, sd, M, N, K, w, s, b, x, out, st);
+        return hipGetLastError();
+    }
+    if (group == 4) {
+        qmv_go<DT, BITS, GS, 4, 1, 1, 4>(batch, sd, M, N, K, w, s, b, x, out, st);
+        return hipGetLastError();
+    }
+    const int mt = qmv_mt_for(M);
     if (mt == 1) {
         const QmvSplit sp = qmv_split_for(M, (long long)N * batch, K, BITS);
         switch (sp.ks * 8 + sp.rg) {
@@ -632,36 +640,37 @@ static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const 
 
 template <int DT, int BITS>
 static hipError_t qmv_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
-                         QmxStrides sd, int M, int N, int K, int gs, hipStream_t st) {
+                         QmxStrides sd, int M, int N, int K, int gs, int group, hipStream_t st) {
     switch (gs) {
-        case 32: return qmv_mt<DT, BITS, 32>(w, s, b, x, out, batch, sd, M, N, K, st);
-        case 64: return qmv_mt<DT, BITS, 64>(w, s, b, x, out, batch, sd, M, N, K, st);
-        default: return qmv_mt<DT, BITS, 128>(w, s, b, x, out, batch, sd, M, N, K, st);
+        case 32: return qmv_mt<DT, BITS, 32>(w, s, b, x, out, batch, sd, M, N, K, group, st);
+        case 64: return qmv_mt<DT, BITS, 64>(w, s, b, x, out, batch, sd, M, N, K, group, st);
+        default: return qmv_mt<DT, BITS, 128>(w, s, b, x, out, batch, sd, M, N, K, group, st);
     }
 }
 
 template <int DT>
 static hipError_t qmv_bits(const uint32_t* w, const void* s, const void* b, const void* x, void* out, int batch,
-                           QmxStrides sd, int M, int N, int K, int bits, int gs, hipStream_t st) {
+                           QmxStrides sd, int M, int N, int K, int bits, int gs, int group, hipStream_t st) {
     switch (bits) {
-        case 1: return qmv_gs<DT, 1>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        case 2: return qmv_gs<DT, 2>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        case 3: return qmv_gs<DT, 3>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        case 4: return qmv_gs<DT, 4>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        case 5: return qmv_gs<DT, 5>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        case 6: return qmv_gs<DT, 6>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
-        default: return qmv_gs<DT, 8>(w, s, b, x, out, batch, sd, M, N, K, gs, st);
+        case 1: return qmv_gs<DT, 1>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        case 2: return qmv_gs<DT, 2>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        case 3: return qmv_gs<DT, 3>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        case 4: return qmv_gs<DT, 4>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        case 5: return qmv_gs<DT, 5>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        case 6: return qmv_gs<DT, 6>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
+        default: return qmv_gs<DT, 8>(w, s, b, x, out, batch, sd, M, N, K, gs, group, st);
     }
 }
 
 hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                       int batch, QmxStrides sd, int M, int N, int K, int bits, int gs, int dt,
-                      hipStream_t st) {
-    if (M != 1 || !sd.w_index) sd.group = 1;   // grouping is defined for single-row gathers only
+                      hipStream_t st, int group) {
+    // grouping is defined for single-row gathers only, in tiles of 2 or 4 problems
+    if (M != 1 || !sd.w_index || (group != 2 && group != 4)) group = 1;
     switch (dt) {
-        case DT_F32: return qmv_bits<DT_F32>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
-        case DT_F16: return qmv_bits<DT_F16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
-        default: return qmv_bits<DT_BF16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, st);
+        case DT_F32: return qmv_bits<DT_F32>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, group, st);
+        case DT_F16: return qmv_bits<DT_F16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, group, st);
+        default: return qmv_bits<DT_BF16>(w, s, b, x, out, batch, sd, M, N, K, bits, gs, group, st);
     }
 }
 

@@ -229,14 +229,15 @@ int batched_impl(const uint32_t* w_packed, const void* scales, const void* biase
         sd.x = (long long)M * K;
         sd.x_row = K;
     }
+    int group = 1;
     if (sorted && w_index && route == QMX_ROUTE_QMV && M == 1) {
         // a grouped tile addresses its x rows from the first x matrix in 32 bits
         const int g = gather_group(batch, num_w);
-        if (g > 1 && ((long long)(num_x - 1) * sd.x + K) * (long long)elem_bytes(dtype) < (1LL << 31)) sd.group = g;
+        if (g > 1 && ((long long)(num_x - 1) * sd.x + K) * (long long)elem_bytes(dtype) < (1LL << 31)) group = g;
     }
     if (route == QMX_ROUTE_QMV)
         return launch_status(qmx::launch_qmv(w_packed, scales, biases, x, out, batch, sd, M, N, K, bits, group_size,
-                                             dtype, st));
+                                             dtype, st, group));
     if (route == QMX_ROUTE_QMM_T)
         return launch_status(qmx::launch_qmm_t(w_packed, scales, biases, x, out, nullptr, batch, sd, M, N, K, bits,
                                                group_size, dtype, 1, st));

@@ -37,14 +37,11 @@ int qmm_mtiles_for(int M);
 // [batch][M][N] (split-K partials: [S][batch][M][N]).
 // With index arrays (gather), problem i takes weight matrix w_index[i] and x
 // matrix x_index[i] instead of i, each clamped to [0, count - 1].
-// group > 1 (M = 1 with w_index only): one vector-ALU tile serves up to
-// `group` consecutive problems that pick the same weight matrix, as its x rows.
 struct QmxStrides {
     long long w, sb, x, x_row;
     const int* w_index = nullptr;
     const int* x_index = nullptr;
     int num_w = 0, num_x = 0;
-    int group = 1;
 };
 inline QmxStrides unbatched(int K) { return QmxStrides{0, 0, 0, K}; }
 
@@ -66,9 +63,11 @@ struct QmvSplit {
 };
 QmvSplit qmv_split_for(int M, long long rows, int K, int bits);
 
+// group > 1 (M = 1 with w_index only): one tile serves up to `group`
+// consecutive problems that pick the same weight matrix, as its x rows.
 hipError_t launch_qmv(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                       int batch, QmxStrides sd, int M, int N, int K, int bits, int gs, int dt,
-                      hipStream_t st);
+                      hipStream_t st, int group = 1);
 
 // splits == 1: writes `out` in dtype dt.  splits > 1: writes float32
 // partials ws[p][batch][M][N] (the accumulate kernel is launched separately).
