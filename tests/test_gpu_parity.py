@@ -642,3 +642,84 @@ def test_random_sweep(orc, case):
     if route == "splitk":
         splits = int(np.random.Generator(np.random.PCG64(i)).integers(2, min(16, K // 256) + 1))
     check_affine(orc, route, M, N, K, bits, gs, dt, seed=5000 + i, splits=splits)
+
+
+# ---------------------------------------------------------------- graph capture
+def test_graph_replay_matches_eager(orc):
+    """The calls captured once in a HIP graph (as bench.py times them) and the
+    graph replayed three times, with eager work, output clearing and
+    synchronizations between the replays: every replay's outputs equal the
+    eager outputs bit for bit, and the eager outputs match the oracle."""
+    say("graph replay: qmv, split-K qmm, unsplit qmm, sorted gather, q8_0, q4_k")
+    dt = qi.BF16
+    cv = qi.affine_case(1, 200, 1024, 4, 64, dt, seed=3100)
+    cs = qi.affine_case(22, 384, 2048, 4, 64, dt, seed=3101)
+    cu = qi.affine_case(40, 256, 256, 3, 32, dt, seed=3102)
+    args = {k: to_dev(c) for k, c in (("v", cv), ("s", cs), ("u", cu))}
+    route_s = qmx.plan(22, 384, 2048, 4, 64, dt)
+    assert route_s[0] == "qmm_t_splitk", route_s
+    ws = torch.empty(max(1, qmx.qmm_workspace_bytes(22, 384, 2048, 4, 64, dt) // 4), dtype=torch.float32,
+                     device=DEV)
+    wc = [qi.affine_case(1, 128, 512, 4, 64, dt, seed=3110 + e) for e in range(3)]
+    gp = [to_dev(c) for c in wc]
+    gw, gs_, gb = (torch.stack([p[j] for p in gp]) for j in range(3))
+    gx = torch.stack([qmx.storage_tensor(qi.affine_case(1, 32, 512, 4, 64, dt, seed=3120 + j)["x"], dt, DEV)
+                      for j in range(6)])
+    gi_host = [0, 0, 1, 1, 2, 2]
+    gi = torch.tensor(gi_host, dtype=torch.int32, device=DEV)
+    c8 = qi.q8_0_case(64, 1024, seed=3130)
+    c4 = qi.q4_k_case(64, 1024, seed=3131)
+    b8, x8 = qmx.words_tensor(c8["blocks"], DEV), torch.from_numpy(c8["x"]).to(DEV)
+    b4, x4 = qmx.words_tensor(c4["blocks"], DEV), torch.from_numpy(c4["x"]).to(DEV)
+    outs = {
+        "v": torch.empty((1, 200), dtype=torch.bfloat16, device=DEV),
+        "s": torch.empty((22, 384), dtype=torch.bfloat16, device=DEV),
+        "u": torch.empty((40, 256), dtype=torch.bfloat16, device=DEV),
+        "g": torch.empty((6, 1, 128), dtype=torch.bfloat16, device=DEV),
+        "q8": torch.empty(64, dtype=torch.float32, device=DEV),
+        "q4": torch.empty(64, dtype=torch.float32, device=DEV),
+    }
+
+    def step():
+        qmx.qmm(*args["v"], outs["v"], bits=4, group_size=64)
+        qmx.qmm(*args["s"], outs["s"], bits=4, group_size=64, workspace=ws)
+        qmx.qmm(*args["u"], outs["u"], bits=3, group_size=32)
+        qmx.gather_qmm(gw, gs_, gb, gx, gi, None, outs["g"], bits=4, group_size=64, sorted_indices=True)
+        qmx.matvec_q8_0(b8, x8, outs["q8"])
+        qmx.matvec_q4_k(b4, x4, outs["q4"])
+
+    step()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    # the eager outputs against the oracle
+    for k, c, m in (("v", cv, 1), ("s", cs, 22), ("u", cu, 40)):
+        assert_close(out64(eager[k], dt), orc.affine_case(c), dt, orc, what=f"graph eager {k}")
+    for i, e in enumerate(gi_host):
+        c = wc[e]
+        xi = qi.affine_case(1, 32, 512, 4, 64, dt, seed=3120 + i)["x"]
+        ref = orc.affine(c["w"], c["scales"], c["biases"], dt, xi, dt, 1, 128, 512, 4, 64)
+        assert_close(out64(eager["g"], dt)[i], ref, dt, orc, what=f"graph eager gather {i}")
+    assert_close(eager["q8"].cpu().numpy().astype(np.float64), orc.q8_0(c8["blocks"], c8["x"], 64, 1024), qi.F32,
+                 orc, "graph eager q8_0")
+    assert_close(eager["q4"].cpu().numpy().astype(np.float64), orc.q4_k(c4["blocks"], c4["x"], 64, 1024), qi.F32,
+                 orc, "graph eager q4_k")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    junk = torch.randn(512, 512, device=DEV)
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        junk = junk @ junk.T / 512.0             # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), f"replay {rep}: {k}"
