@@ -723,3 +723,33 @@ def test_graph_replay_matches_eager(orc):
         torch.cuda.synchronize()
         for k, v in outs.items():
             assert torch.equal(v.view(torch.uint8), eager[k].view(torch.uint8)), f"replay {rep}: {k}"
+
+
+@pytest.mark.parametrize("sorted_indices", [False, True])
+def test_gather_bench_size(orc, sorted_indices):
+    """The gather workload's own size: 16 problems over 8 weight matrices of
+    2048 x 4096 (4-bit gs 64 bf16, M = 1), each matrix picked twice, in random
+    order or ordered by matrix; sampled columns of every problem against the
+    oracle."""
+    B, E, N, K = 16, 8, 2048, 4096
+    g = torch.Generator(device="cpu")
+    g.manual_seed(3200)
+    picks = (torch.randperm(B, generator=g) % E)
+    if sorted_indices:
+        picks = torch.sort(picks).values
+    w_index = picks.tolist()
+    say("gather bench size", B, E, N, K, "sorted" if sorted_indices else "random", w_index)
+    wc = [qi.affine_case(1, N, K, 4, 64, qi.BF16, seed=3210 + e) for e in range(E)]
+    xc = [qi.affine_case(1, 32, K, 4, 64, qi.BF16, seed=3230 + j)["x"] for j in range(B)]
+    parts = [to_dev(c) for c in wc]
+    w, s, b = (torch.stack([p[j] for p in parts]) for j in range(3))
+    x = torch.stack([qmx.storage_tensor(v, qi.BF16, DEV) for v in xc])
+    wi = torch.tensor(w_index, dtype=torch.int32, device=DEV)
+    y = qmx.gather_qmm(w, s, b, x, wi, bits=4, group_size=64, sorted_indices=sorted_indices)
+    torch.cuda.synchronize()
+    got = out64(y, qi.BF16)
+    cols = sample_cols(N, 192, seed=3240)
+    for i, e in enumerate(w_index):
+        c = wc[e]
+        ref = orc.affine(c["w"], c["scales"], c["biases"], qi.BF16, xc[i], qi.BF16, 1, N, K, 4, 64, cols=cols)
+        assert_close(got[i][:, cols], ref, qi.BF16, orc, what=f"gather bench-size problem {i}: W{e}")
