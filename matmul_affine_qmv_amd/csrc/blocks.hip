@@ -3,7 +3,9 @@
 // Formats and arithmetic follow page "hanzo-kernel src/quant.rs" (Q8_0
 // packed layout: 9 words per 32 weights; Q4_K: 144-byte super-blocks with
 // 6-bit sub-block scales and mins).  Both kernels are weight-bandwidth
-// bound.  A work-group of 4 waves owns 16 output rows, 4 per wave, and walks
+// bound.  A work-group of 4 waves owns 4 output rows per wave (5 for Q4_K,
+// whose register use allows 3 waves per SIMD: 5 rows fit N = 14336 in one
+// generation of resident work-groups), and walks
 // K in rounds of 2048 values: the round's float32 x is loaded once per
 // work-group (two 16-byte loads per thread) and shared through LDS, so x
 // costs a quarter of a weight row's worth of loads instead of as much as the
@@ -14,7 +16,8 @@
 
 namespace qmx {
 
-constexpr int BLK_ROWS = 4;                         // output rows per wave
+constexpr int Q8_ROWS = 4;                          // output rows per wave: Q8_0
+constexpr int Q4K_ROWS = 5;                         // and Q4_K (one generation of waves at N = 14336)
 constexpr int BLK_WAVES = 4;                        // waves per work-group
 constexpr int BLK_THREADS = 64 * BLK_WAVES;
 constexpr int BLK_ROUND = 2048;                     // x values per round (8 KB)
@@ -78,18 +81,19 @@ __device__ __forceinline__ void blk_rounds(const float* __restrict__ x, int K, i
     }
 }
 
-__device__ __forceinline__ void blk_store(float (&acc)[BLK_ROWS], int lane, int n0, int N, float* __restrict__ out) {
+template <int ROWS>
+__device__ __forceinline__ void blk_store(float (&acc)[ROWS], int lane, int n0, int N, float* __restrict__ out) {
     // the same fixed butterfly as wave_sum, step-major so the rows' exchanges of a
     // step share one wait
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
-        for (int r = 0; r < BLK_ROWS; ++r) acc[r] += __shfl_xor(acc[r], off, 64);
+        for (int r = 0; r < ROWS; ++r) acc[r] += __shfl_xor(acc[r], off, 64);
     float mine = 0.f;
 #pragma unroll
-    for (int r = 0; r < BLK_ROWS; ++r)
+    for (int r = 0; r < ROWS; ++r)
         if (lane == r) mine = acc[r];
-    if (lane < BLK_ROWS && n0 + lane < N) out[n0 + lane] = mine;
+    if (lane < ROWS && n0 + lane < N) out[n0 + lane] = mine;
 }
 
 // ---------------------------------------------------------------- Q8_0
@@ -102,16 +106,16 @@ __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __res
                                                            float* __restrict__ out, int N, int K) {
     __shared__ u32x4 xl[2][BLK_ROUND / 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * Q8_ROWS;
     const int nb = K / 32;
-    float acc[BLK_ROWS] = {};
+    float acc[Q8_ROWS] = {};
 
-    struct WS { uint32_t w[BLK_ROWS][9]; };
+    struct WS { uint32_t w[Q8_ROWS][9]; };
     if (nb > 0) {
         auto load = [&](int rd, WS& st) {
             const int b = min(64 * rd + lane, nb - 1);
 #pragma unroll
-            for (int r = 0; r < BLK_ROWS; ++r) {
+            for (int r = 0; r < Q8_ROWS; ++r) {
                 const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 9;
 #pragma unroll
                 for (int j = 0; j < 9; ++j) st.w[r][j] = blk[j];
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __res
 #pragma unroll
             for (int i = 0; i < 32; ++i) xs += xv[i];
 #pragma unroll
-            for (int r = 0; r < BLK_ROWS; ++r) {
+            for (int r = 0; r < Q8_ROWS; ++r) {
                 const float d = f16_bits_to_f32(st.w[r][0] & 0xffffu);
                 float s = 0.f;
 #pragma unroll
@@ -183,17 +187,17 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = lane >> 3, part = lane & 7;
     const int g = part >> 1, t0 = (part & 1) * 16;
-    const int n0 = (blockIdx.x * BLK_WAVES + wave) * BLK_ROWS;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * Q4K_ROWS;
     const int nb = K / 256;
     const Q4kFields f_lo = q4k_fields(2 * g), f_hi = q4k_fields(2 * g + 1);
-    float acc[BLK_ROWS] = {};
+    float acc[Q4K_ROWS] = {};
 
-    struct WS { u32x4 hdr[BLK_ROWS], qw[BLK_ROWS]; };
+    struct WS { u32x4 hdr[Q4K_ROWS], qw[Q4K_ROWS]; };
     if (nb > 0) {
         auto load = [&](int rd, WS& st) {
             const int b = min(8 * rd + slot, nb - 1);
 #pragma unroll
-            for (int r = 0; r < BLK_ROWS; ++r) {
+            for (int r = 0; r < Q4K_ROWS; ++r) {
                 const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 36;
                 st.hdr[r] = *reinterpret_cast<const u32x4*>(blk);
                 st.qw[r] = *reinterpret_cast<const u32x4*>(blk + 4 + 4 * part);
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
 #pragma unroll
             for (int i = 0; i < 16; ++i) { xsl += xlo[i]; xsh += xhi[i]; }
 #pragma unroll
-            for (int r = 0; r < BLK_ROWS; ++r) {
+            for (int r = 0; r < Q4K_ROWS; ++r) {
                 const float d = f16_bits_to_f32(st.hdr[r].x & 0xffffu);
                 const float dmin = f16_bits_to_f32(st.hdr[r].x >> 16);
                 uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
@@ -243,13 +247,13 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
 }
 
 hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
-    const dim3 grid((N + BLK_WAVES * BLK_ROWS - 1) / (BLK_WAVES * BLK_ROWS));
+    const dim3 grid((N + BLK_WAVES * Q8_ROWS - 1) / (BLK_WAVES * Q8_ROWS));
     hipLaunchKernelGGL(q8_0_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
 }
 
 hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
-    const dim3 grid((N + BLK_WAVES * BLK_ROWS - 1) / (BLK_WAVES * BLK_ROWS));
+    const dim3 grid((N + BLK_WAVES * Q4K_ROWS - 1) / (BLK_WAVES * Q4K_ROWS));
     hipLaunchKernelGGL(q4_k_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
 }
