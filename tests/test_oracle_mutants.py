@@ -22,6 +22,10 @@ MUTANTS = {
                            "acc += value_at(x, x_dt, (size_t)k * M + m) * wk;"),
     "scale_bias_swapped": ("double wk = value_at(s, sb_dt, (size_t)n * G + g) * (double)code_at(row, k, bits)\n                      + value_at(b, sb_dt, (size_t)n * G + g);",
                            "double wk = value_at(b, sb_dt, (size_t)n * G + g) * (double)code_at(row, k, bits)\n                      + value_at(s, sb_dt, (size_t)n * G + g);"),
+    "split_end_inclusive": ("for (long k = (long)g0 * gs; k < (long)g1 * gs; ++k) {",
+                            "for (long k = (long)g0 * gs; k < (long)(g1 < G ? g1 + 1 : g1) * gs; ++k) {"),
+    "hoisted_sum_x_per_row": ("        for (int g = 0; g < G; ++g) {\n            double qx = 0.0, xs = 0.0;",
+                              "        double xs = 0.0;\n        for (int g = 0; g < G; ++g) {\n            double qx = 0.0;"),
     "i8_no_sign_extension": ("return v >= 128 ? (int)v - 256 : (int)v;", "return (int)v;"),
     "i8_block_scale_shifted": ("acc += (double)wd[(long)n * nb + b] * (double)dot;",
                                "acc += (double)wd[(long)n * nb + (b + 1) % nb] * (double)dot;"),
