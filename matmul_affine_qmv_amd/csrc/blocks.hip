@@ -3,9 +3,10 @@
 // Formats and arithmetic follow page "hanzo-kernel src/quant.rs" (Q8_0
 // packed layout: 9 words per 32 weights; Q4_K: 144-byte super-blocks with
 // 6-bit sub-block scales and mins).  Both kernels are weight-bandwidth
-// bound.  A work-group of 4 waves owns 4 output rows per wave (5 for Q4_K,
-// whose register use allows 3 waves per SIMD: 5 rows fit N = 14336 in one
-// generation of resident work-groups), and walks
+// bound.  A work-group of 4 waves owns 8 output rows per wave for Q8_0 and
+// 5 for Q4_K (both at 3 waves per SIMD, so N = 14336 runs in one generation
+// of resident work-groups; more rows per wave keep more of a wave's loads in
+// flight per round trip), and walks
 // K in rounds of 2048 values: the round's float32 x is loaded once per
 // work-group (two 16-byte loads per thread) and shared through LDS, so x
 // costs a quarter of a weight row's worth of loads instead of as much as the
@@ -16,8 +17,8 @@
 
 namespace qmx {
 
-constexpr int Q8_ROWS = 4;                          // output rows per wave: Q8_0
-constexpr int Q4K_ROWS = 5;                         // and Q4_K (one generation of waves at N = 14336)
+constexpr int Q8_ROWS = 8;                          // output rows per wave: Q8_0
+constexpr int Q4K_ROWS = 5;                         // and Q4_K
 constexpr int BLK_WAVES = 4;                        // waves per work-group
 constexpr int BLK_THREADS = 64 * BLK_WAVES;
 constexpr int BLK_ROUND = 2048;                     // x values per round (8 KB)
