@@ -6,9 +6,11 @@
 // group of four is one hardware 4-way integer dot, a block's integer sum is
 // exact, and out[n] = sum_b wd[n,b] * dot_b is accumulated in float32.
 //
-// gfx950 mapping: a wave owns 4 rows and lane l takes blocks l, l + 64, ... of
+// gfx950 mapping: a wave owns 2 rows and lane l takes blocks l, l + 64, ... of
 // them, so a load instruction reads 2 KB contiguous per row; the block's 32
-// activations are loaded once per lane and used by the 4 rows.  Each block is
+// activations are loaded once per lane and used by both rows.  A wave keeps
+// one round of loads in flight, so many small waves (8 per SIMD, the whole
+// grid resident at once) hide the round trips better than fewer wide ones.  Each block is
 // eight v_dot4_i32_i8 into an int32 (|sum| <= 32 * 128 * 128), then one float32
 // fma with the row's block scale.  All loads are buffer loads whose per-round
 // advance is a scalar offset.  The rows' sums end in the fixed xor butterfly,
@@ -18,7 +20,7 @@
 
 namespace qmx {
 
-constexpr int I8_ROWS = 4;     // rows per wave
+constexpr int I8_ROWS = 2;     // rows per wave
 constexpr int I8_WAVES = 4;    // waves per work-group
 
 __device__ __forceinline__ int dot8x4(const u32x4& a, const u32x4& b, int c) {
