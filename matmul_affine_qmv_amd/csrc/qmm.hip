@@ -5,10 +5,10 @@
 namespace qmx {
 
 // 16-row x fragments per tile: the smallest of 1, 2, 3, 4, 6, 8 that covers
-// M in one tile, else tiles of at most 8 fragments spread evenly over M.
-int qmm_mt_for(int M) {
+// the tile's share of M (tiles spread evenly over M).
+int qmm_mt_for(int M, int mtiles) {
     static const int choices[] = {1, 2, 3, 4, 6, 8};
-    const int tiles = qmm_mtiles_for(M);
+    const int tiles = mtiles > 0 ? mtiles : 1;
     const int rows = (M + tiles - 1) / tiles;
     const int frags = (rows + 15) / 16;
     for (int c : choices)
@@ -19,8 +19,23 @@ int qmm_mt_for(int M) {
 // Tiles of at most 64 rows up to M = 192 (MT <= 4: measured 15-20% faster per
 // call at M = 85 and 128 than one tile of 6 or 8 fragments, as the larger tiles
 // lose ring depth and staged scales to LDS); 128-row tiles beyond, where the
-// fewer, fuller tiles fill the chip better.
-int qmm_mtiles_for(int M) { return M <= 192 ? (M + 63) / 64 : (M + 127) / 128; }
+// fewer, fuller tiles fill the chip better.  When 128-row tiles alone leave
+// compute units idle, 64-row tiles are taken if, with the policy's K split,
+// they launch at least as many work-groups.  Measured at N = K = 4096
+// (policy route, per call): M = 384 33.7 against 37.2 us, M = 512 36.6
+// against 39.7 us, and (N = 1024, M = 512) 19.7 against 25.1 us; at M = 257
+// the 64-row tiles launch fewer work-groups (160 unsplit against 96 x 2) and
+// were slower (34.4 against 31.5 us); at M = 1024 and 2048, where 128-row
+// tiles fill the chip, 15% slower.
+int qmm_mtiles_for(int M, long long col_tiles, int cus, int K) {
+    const int t64 = (M + 63) / 64;
+    if (M <= 192) return t64;
+    const int t128 = (M + 127) / 128;
+    if (cus <= 0 || col_tiles * t128 >= cus) return t128;
+    const long long wg64 = col_tiles * t64 * qmm_policy_splits(col_tiles * t64, K, cus);
+    const long long wg128 = col_tiles * t128 * qmm_policy_splits(col_tiles * t128, K, cus);
+    return wg64 >= wg128 ? t64 : t128;
+}
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int bits, int gs,

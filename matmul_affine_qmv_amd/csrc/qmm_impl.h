@@ -598,9 +598,9 @@ void qmm_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const vo
 
 template <int DT, int BITS, int GS, int MT>
 hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
-                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
+                         float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, int mtiles,
+                         hipStream_t st) {
     const int ntiles = (N + QMM_BN - 1) / QMM_BN;
-    const int mtiles = qmm_mtiles_for(M);
     const int total = ntiles * mtiles * splits;
     const int per_xcd = (total + 7) / 8;
     const dim3 grid(8 * per_xcd, batch);
@@ -629,14 +629,17 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
 template <int DT, int BITS, int GS>
 hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
-    switch (qmm_mt_for(M)) {
-        case 1: return qmm_launch_mt<DT, BITS, GS, 1>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
-        case 2: return qmm_launch_mt<DT, BITS, GS, 2>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
-        case 3: return qmm_launch_mt<DT, BITS, GS, 3>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
-        case 4: return qmm_launch_mt<DT, BITS, GS, 4>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
-        case 6: return qmm_launch_mt<DT, BITS, GS, 6>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
-        default: return qmm_launch_mt<DT, BITS, GS, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, st);
+    const int mt = qmm_mtiles_for(M, (long long)((N + QMM_BN - 1) / QMM_BN) * batch, device_cu_count(), K);
+#define QMM_MT(MT_) qmm_launch_mt<DT, BITS, GS, MT_>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, mt, st)
+    switch (qmm_mt_for(M, mt)) {
+        case 1: return QMM_MT(1);
+        case 2: return QMM_MT(2);
+        case 3: return QMM_MT(3);
+        case 4: return QMM_MT(4);
+        case 6: return QMM_MT(6);
+        default: return QMM_MT(8);
     }
+#undef QMM_MT
 }
 
 template <int BITS>

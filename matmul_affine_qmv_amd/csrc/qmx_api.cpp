@@ -64,7 +64,8 @@ int check_qmm(const uint32_t* w, const void* s, const void* b, const void* x, vo
     if (rc) return rc;
     if (dtype == QMX_F32) return QMX_ERR_DTYPE;
     if (K % QMM_KB != 0) return QMX_ERR_SHAPE;
-    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * (M > 0 ? qmx::qmm_mtiles_for(M) : 0);
+    // the largest tiling the launcher may choose
+    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * (M > 0 ? (M + 63) / 64 : 0);
     if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
     if (M == 0 || N == 0) return QMX_OK;
     return check_affine_ptrs(w, s, b, x, out, K, dtype, 16, 16);
@@ -124,20 +125,11 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
         *splits = 1;
         return QMX_OK;
     }
-    const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M) * batch;
-    *route = QMX_ROUTE_QMM_T;
-    *splits = 1;
-    // below 8 K blocks the partitions are too short to repay the accumulate
-    // (measured: K = 512 and 768 unsplit 10-15% faster at M = 16, N = 4096)
-    if (K < 8 * QMM_KB || tiles >= num_cus || tiles == 0) return QMX_OK;
-    // as many partitions as keep every work-group of the launch resident at once
-    long long s = num_cus / tiles;
-    const int cap = max_splits_for(K) < kPolicyMaxSplits ? max_splits_for(K) : kPolicyMaxSplits;
-    if (s > cap) s = cap;
-    if (s >= 2) {
-        *route = QMX_ROUTE_QMM_T_SPLITK;
-        *splits = (int)s;
-    }
+    const long long col_tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
+    const long long tiles = col_tiles * qmx::qmm_mtiles_for(M, col_tiles, num_cus, K);
+    const int s = qmx::qmm_policy_splits(tiles, K, num_cus);
+    *route = s >= 2 ? QMX_ROUTE_QMM_T_SPLITK : QMX_ROUTE_QMM_T;
+    *splits = s;
     return QMX_OK;
 }
 
@@ -207,7 +199,7 @@ int batched_impl(const uint32_t* w_packed, const void* scales, const void* biase
         if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
         if ((long long)((M + qmx::qmv_mt_for(M) - 1) / qmx::qmv_mt_for(M)) > 65535) return QMX_ERR_SHAPE;
     } else {
-        const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * qmx::qmm_mtiles_for(M);
+        const long long tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * ((M + 63) / 64);
         if (tiles * splits + 8 > INT_MAX) return QMX_ERR_SHAPE;
     }
     const bool copy_x = K > 0 && x_needs_copy(x, x_batch_stride, x_row_stride, dtype);
@@ -249,6 +241,21 @@ int batched_impl(const uint32_t* w_packed, const void* scales, const void* biase
 }
 
 }  // namespace
+
+namespace qmx {
+int device_cu_count() { return device_cus(); }
+
+int qmm_policy_splits(long long tiles, int K, int cus) {
+    // below 8 K blocks the partitions are too short to repay the accumulate
+    // (measured: K = 512 and 768 unsplit 10-15% faster at M = 16, N = 4096)
+    if (K < 8 * QMM_KB || tiles >= cus || tiles <= 0) return 1;
+    // as many partitions as keep every work-group of the launch resident at once
+    long long s = cus / tiles;
+    const int cap = max_splits_for(K) < kPolicyMaxSplits ? max_splits_for(K) : kPolicyMaxSplits;
+    if (s > cap) s = cap;
+    return s >= 2 ? (int)s : 1;
+}
+}  // namespace qmx
 
 extern "C" {
 

@@ -26,9 +26,17 @@ constexpr int QMM_NB = 2;
 constexpr int QMM_BN = QMM_WAVES_N * QMM_NB * 16;
 constexpr int QMM_KB = 128;
 constexpr int QMM_THREADS = 2 * QMM_WAVES_N * 64;
-// 16-row x fragments per tile chosen for M (1, 2, 3, 4, 6 or 8) and the tile count.
-int qmm_mt_for(int M);
-int qmm_mtiles_for(int M);
+// Tiles along M for M rows of x when `col_tiles` column tiles (N tiles times
+// the batch) share `cus` compute units over K columns, and the 16-row x
+// fragments per tile (1, 2, 3, 4, 6 or 8) for M rows in `mtiles` tiles.
+// Tiles never exceed (M + 63) / 64.
+int qmm_mtiles_for(int M, long long col_tiles, int cus, int K);
+int qmm_mt_for(int M, int mtiles);
+// K partitions the dispatch policy gives `tiles` output tiles on `cus`
+// compute units (1: unsplit).
+int qmm_policy_splits(long long tiles, int K, int cus);
+// Compute units of the current device (cached per device), or -1.
+int device_cu_count();
 
 // A batch of independent problems of one shape: problem i reads weights
 // `i * w` words, scales and biases `i * sb` elements and x `i * x` elements

@@ -170,7 +170,11 @@ def test_block_validation():
     (128, 4096, 4096, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 N tiles
     (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
     (56, 5120, 17408, BF16, "qmm_t_splitk", 6),      # floor(256 / 40 tiles)
-    (512, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 4 M tiles x 32 N tiles = 128 tiles
+    (512, 4096, 4096, BF16, "qmm_t", 1),             # 64-row tiles: 8 M tiles x 32 N tiles fill 256 CUs
+    (1024, 4096, 4096, BF16, "qmm_t", 1),            # 128-row tiles: 8 x 32
+    (512, 1024, 4096, BF16, "qmm_t_splitk", 4),      # 64-row tiles, 8 x 8 = 64 tiles: 4 partitions
+    (257, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 128-row tiles: 3 x 32 split 2 = 192 groups (64-row: 160)
+    (384, 4096, 4096, BF16, "qmm_t", 1),             # 64-row tiles: 6 x 32 = 192 groups, as many as 3 x 32 split 2
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
     (8, 4096, 4096, F16, "qmm_t_splitk", 8),
     (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
