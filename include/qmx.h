@@ -205,8 +205,10 @@ int qmx_matvec_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, fl
  * 256).  Routes: float32 activations, K % 128 != 0 and M = 1 take qmx_qmv;
  * M = 2..7 takes qmx_qmv unless a cost estimate (qmv's vector work grows
  * with M, the matrix route with the weight bytes) favours the matrix cores;
- * otherwise qmx_qmm_t, split along K when its tiles leave compute units idle.
- * Performs no HIP call.  Returns QMX_OK or a validation status.
+ * otherwise qmx_qmm_t, split along K when its tiles leave compute units idle
+ * (tiles of 128 columns by up to 64 rows of x; above M = 192 by up to 128
+ * rows when those fill the device or launch more work-groups after the
+ * split).  Performs no HIP call.  Returns QMX_OK or a validation status.
  * route/splits: host pointers.
  */
 int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus,
