@@ -753,3 +753,14 @@ def test_gather_bench_size(orc, sorted_indices):
         c = wc[e]
         ref = orc.affine(c["w"], c["scales"], c["biases"], qi.BF16, xc[i], qi.BF16, 1, N, K, 4, 64, cols=cols)
         assert_close(got[i][:, cols], ref, qi.BF16, orc, what=f"gather bench-size problem {i}: W{e}")
+
+
+@pytest.mark.parametrize("M,N", [(257, 4096), (384, 4096), (512, 1024), (300, 1024)])
+def test_qmm_large_m_tilings(orc, M, N):
+    """The policy above M = 192: 128-row tiles split in 2 (M = 257), 64-row
+    tiles unsplit (M = 384) and 64-row tiles split (N = 1024), sampled
+    columns of every row against the oracle, reruns bit-identical."""
+    route = qmx.plan(M, N, 4096, 4, 64, qi.BF16)
+    say("large-M tiling", M, N, route)
+    check_affine(orc, "qmm", M, N, 4096, 4, 64, qi.BF16, seed=3300 + M + N, cols=sample_cols(N, 96, M + N),
+                 reruns=1)
