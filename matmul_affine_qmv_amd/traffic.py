@@ -36,9 +36,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def source_digest() -> str:
-    """sha256 over the kernel sources (csrc/*), in name order."""
+    """sha256 over the library's kernel sources (csrc/*, without the
+    calibration kernels, which are not part of it), in name order."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        if os.path.basename(path).startswith("calib"):
+            continue
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())

@@ -38,6 +38,26 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(qmx._EXPORTS), "binding and header disagree"
 
 
+def test_calibration_library_exports_its_header():
+    """libqmx_calib.so (streaming-read, copy, matrix-core and empty kernels used
+    beside the measurements) exports exactly what include/qmx_calib.h declares."""
+    from matmul_affine_qmv_amd import calib
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qmx_calib.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(qmxc_[a-z0-9_]+)\s*\(", text)))
+    assert names == sorted(calib.EXPORTS)
+    raw = ctypes.CDLL(calib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    L = calib.lib()
+    # argument errors return before any HIP call
+    assert L.qmxc_read(None, 16, None, 0, 1, None) == -1
+    assert L.qmxc_read(16, 17, 16, 0, 1, None) == -1
+    assert L.qmxc_copy(16, 32, 16, 0, None) == -1
+    assert L.qmxc_mfma(None, 1, 1, 32, None) == -1
+    assert L.qmxc_mfma(16, 1, 1, 8, None) == -1
+    assert L.qmxc_empty(0, None) == -1
+
+
 def test_version_and_strerror():
     assert qmx.api_version() == 1
     for code in range(-10, 1):

@@ -55,14 +55,37 @@ def test_batched_and_gather_bytes():
 
 
 def test_split_kernels_bytes():
-    """The partial kernel moves the inputs plus S*M*N float32 partials; the
-    accumulate kernel reads the partials and writes the 16-bit output."""
+    """Algorithmic bytes of a split call are the call's own: the partial kernel
+    is credited with the inputs, the accumulate with the 16-bit output, and the
+    S*M*N float32 partials count for neither (they show up as lost efficiency
+    and are reported on their own)."""
     c = bench.affine("qmm", 56, 5120, 17408)
-    (lp, _, bp, fp, mp), (la, _, ba, fa, ma) = bench.kernels_of(c, "qmm_t_splitk", 6)
-    parts = 6 * 56 * 5120 * 4
-    assert bp == 52_658_176 - 56 * 5120 * 2 + parts == 58_966_016
-    assert ba == parts + 56 * 5120 * 2
+    (lp, fnp, bp, fp, mp), (la, fna, ba, fa, ma) = bench.kernels_of(c, "qmm_t_splitk", 6)
+    assert bp == 52_658_176 - 56 * 5120 * 2 == 52_084_736
+    assert ba == 56 * 5120 * 2
+    assert bp + ba == bench.alg_bytes(c)
     assert fp == 2 * 56 * 5120 * 17408 and fa == 0 and mp and not ma
+    assert fnp is not None and fna is None   # the accumulate is the call's time less the partial kernel's
+    assert bench.partial_bytes(c, "qmm_t_splitk", 6) == 2 * 6 * 56 * 5120 * 4
+    assert bench.partial_bytes(c, "qmm_t", 1) == 0
+
+
+def test_forced_split_workload_keeps_256_columns_per_partition():
+    calls = bench.WORKLOADS["qmm_splits_4bit_gs64_bf16"]
+    for c in calls:
+        if c["route"] == "splitk":
+            assert c["splits"] in (2, 3, 4) and c["K"] >= 512 and c["K"] // c["splits"] >= 256
+    got = {(c["K"], c["splits"]) for c in calls if c["route"] == "splitk"}
+    assert (256, 2) not in got and (17408, 4) in got and (2048, 3) in got
+    # every shape also runs unsplit
+    assert len([c for c in calls if c["route"] == "qmm_t"]) == len(bench.QMM_SHAPES)
+
+
+def test_sweep_workload_covers_the_grid():
+    calls = bench.WORKLOADS["sweep_4096"]
+    assert len(calls) == 3 * 3 * 2 * 5
+    assert {(c["bits"], c["gs"], c["dtype"], c["M"]) for c in calls} == {
+        (b, g, d, m) for b in (2, 4, 8) for g in (32, 64, 128) for d in (F16, BF16) for m in (1, 8, 33, 128, 257)}
 
 
 def test_roofline_bound_choice():
