@@ -68,7 +68,8 @@ typedef enum qmx_status {
     QMX_ERR_WORKSPACE = -7,  /* split-K workspace NULL or too small                */
     QMX_ERR_SPLITS = -8,     /* split count out of range for this K                */
     QMX_ERR_LAUNCH = -9,     /* the HIP runtime rejected a launch                  */
-    QMX_ERR_DEVICE = -10     /* no usable HIP device                               */
+    QMX_ERR_DEVICE = -10,    /* no usable HIP device                               */
+    QMX_ERR_SCRATCH = -11    /* partials larger than qmx_qmm_t_splitk_noalloc holds */
 } qmx_status;
 
 typedef enum qmx_route {
@@ -157,6 +158,26 @@ int qmx_splitk_accumulate(const void* workspace, void* out, int M, int N, int sp
 /* Bytes of float32 partials qmx_qmm_t_splitk needs: splits * M * N * 4
  * (0 for negative arguments). */
 size_t qmx_splitk_workspace_bytes(int M, int N, int splits);
+
+/* Size of the per-device scratch array of qmx_qmm_t_splitk_noalloc. */
+#define QMX_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* qmx_qmm_t_splitk_noalloc -- qmx_qmm_t_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, partitions, results and
+ * errors as qmx_qmm_t_splitk without the workspace: the float32 partials go
+ * into a scratch array of QMX_NOALLOC_SCRATCH_BYTES that this library holds
+ * on each device it runs on until the process ends (16 MiB covers every
+ * split qmx_plan picks on a 256-CU device: splits * tiles <= CUs, a tile at
+ * most 128 x 128 floats).  QMX_ERR_SCRATCH when splits * M * N * 4 exceeds
+ * it.  Nothing is allocated or freed: the array's device address is looked
+ * up once per device (QMX_ERR_DEVICE if that fails).  Every call on one
+ * device shares that device's array and nothing in it needs clearing; calls
+ * that overlap on one device (e.g. on two streams) race on it and must be
+ * ordered by the caller. */
+int qmx_qmm_t_splitk_noalloc(const uint32_t* w_packed, const void* scales, const void* biases,
+                             const void* x, void* out, int M, int N, int K, int bits, int group_size,
+                             int dtype, int splits, void* stream);
 
 /* qmx_matvec_q8_0 -- Q8_0 block matvec, M = 1 (page "hanzo-kernel
  * src/quant.rs": Q8_0 matvec and its packed layout).

@@ -40,6 +40,7 @@ _EXPORTS = {
                            + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "qmx_splitk_accumulate": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4 + [ctypes.c_void_p]),
     "qmx_splitk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 3),
+    "qmx_qmm_t_splitk_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [ctypes.c_void_p]),
     "qmx_matvec_q8_0": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
     "qmx_matvec_q4_k": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
     "qmx_matvec_q8_i8": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
@@ -193,6 +194,17 @@ def qmm_t_splitk(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64
                                   bits, group_size, _dtype_code(x), splits, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(x)),
            "qmx_qmm_t_splitk")
+    return out
+
+
+def qmm_t_splitk_noalloc(w_packed, scales, biases, x, out=None, *, bits=4, group_size=64, splits=2):
+    """out[M, N] via qmx_qmm_t_splitk_noalloc: qmm_t_splitk with the partials in
+    the library's per-device scratch array (no workspace, nothing allocated
+    beyond `out` when the caller passes none)."""
+    M, N, K, out = _affine_args(w_packed, scales, biases, x, bits, group_size, out)
+    _check(lib().qmx_qmm_t_splitk_noalloc(_ptr(w_packed), _ptr(scales), _ptr(biases), _ptr(x), _ptr(out), M, N, K,
+                                          bits, group_size, _dtype_code(x), splits, _stream(x)),
+           "qmx_qmm_t_splitk_noalloc")
     return out
 
 
@@ -462,7 +474,7 @@ def tensor_bits(t: torch.Tensor):
     return t.numpy()
 
 
-__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm", "qmm_batched", "gather_qmm", "plan", "plan_batched",
+__all__ = ["qmv", "qmm_t", "qmm_t_splitk", "qmm_t_splitk_noalloc", "qmm", "qmm_batched", "gather_qmm", "plan", "plan_batched",
            "matvec_q8_0",
            "matvec_q4_k", "matvec_q8_i8",
            "splitk_workspace_bytes", "qmm_workspace_bytes", "strerror", "api_version", "lib",

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libqmx.so")
 CALIB_LIB = os.path.join(PKG, "libqmx_calib.so")
 
 SOURCES = ["qmv.hip", "qmm_b4.hip", "qmm_b8.hip", "qmm_b2.hip", "qmm_b3.hip", "qmm_b6.hip", "qmm_b5.hip",
-           "qmm_b1.hip", "blocks.hip", "q8_i8.hip", "qmm.hip", "qmx_api.cpp"]
+           "qmm_b1.hip", "blocks.hip", "q8_i8.hip", "qmm.hip", "qmx_api.cpp", "noalloc.hip"]
 CALIB_SOURCES = ["calib.hip"]
 ARCH = "gfx950"
 

@@ -274,6 +274,7 @@ const char* qmx_strerror(int status) {
         case QMX_ERR_SPLITS: return "split count out of range for this K";
         case QMX_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
         case QMX_ERR_DEVICE: return "no usable HIP device";
+        case QMX_ERR_SCRATCH: return "split-K partials exceed the scratch array of qmx_qmm_t_splitk_noalloc";
         default: return "unknown status";
     }
 }
