@@ -211,19 +211,24 @@ def test_splitk_partials_match_partition_oracle(orc):
 def test_partials_and_accumulate_entry_points(orc, bits, gs, dt):
     """qmx_qmm_t_partials writes exactly the partition partials qmx_qmm_t_splitk
     leaves in its workspace, and qmx_splitk_accumulate of those partials gives
-    qmx_qmm_t_splitk's output bit for bit."""
+    qmx_qmm_t_splitk's output bit for bit; the workspace's contents on entry
+    (random bytes here, then the first call's) do not matter."""
     M, N, K, S = 33, 384, 2560, 4
     say("partials + accumulate", M, N, K, bits, gs, dt, S)
     c = qi.affine_case(M, N, K, bits, gs, dt, seed=1600 + bits + gs)
     w, s, b, x = to_dev(c)
-    ws_a = torch.full((S * M * N,), float("nan"), dtype=torch.float32, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(1650 + bits + gs)
+    words = qmx.splitk_workspace_bytes(M, N, S) // 4
+    ws_a = torch.randint(-2**31, 2**31 - 1, (words,), generator=g, dtype=torch.int32).to(DEV).view(torch.float32)
     y = qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=S, workspace=ws_a)
+    y2 = qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=S, workspace=ws_a)
     parts = qmx.qmm_t_partials(w, s, b, x, bits=bits, group_size=gs, splits=S)
     out = torch.empty_like(y)
     qmx.splitk_accumulate(parts, out, S)
     torch.cuda.synchronize()
-    assert torch.equal(parts.view(-1).view(torch.int32), ws_a.view(torch.int32))
+    assert torch.equal(parts.reshape(-1).view(torch.int32), ws_a.view(torch.int32))
     assert torch.equal(out.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
     nkb = K // 128
     host = parts.cpu().numpy().astype(np.float64)
     for p in range(S):
