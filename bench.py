@@ -447,6 +447,21 @@ def calibrate(dev, sizes, calls, repeats):
         us, _ = time_per_launch(lambda _, s=shape: calib.mfma(out, iters, 16 * cus, s), [None, None], calls=10,
                                 repeats=repeats)
         res[f"mfma_bf16_tflops_{shape}x{shape}"] = calib.mfma_flops(iters, 16 * cus) / us / 1e6
+    # Matrix-core / vector-ALU co-issue, two waves per SIMD: cycles per SIMD (at
+    # the 2.4 GHz peak clock) for one 32x32x16 MFMA followed by F float FMAs,
+    # against the MFMA alone and the FMAs alone.
+    co, co_iters = {}, 1000
+    for f in calib.MFMA_VALU_FMAS:
+        row = {}
+        for with_mfma in (True, False):
+            if f == 0 and not with_mfma:
+                continue
+            us, _ = time_per_launch(lambda _, f=f, w=with_mfma: calib.mfma_valu(out, co_iters, 2 * cus, f, w),
+                                    [None, None], calls=10, repeats=repeats)
+            # 2*cus work-groups of 4 waves: two waves per SIMD, 4 rounds per iteration
+            row["mfma_plus_fma" if with_mfma else "fma_only"] = round(us * 1e-6 * 2.4e9 / (co_iters * 4 * 2), 1)
+        co[f"fma_per_mfma_{f}"] = row
+    res["mfma_valu_cycles_per_simd_round"] = co
     us, _ = time_per_launch(lambda _: calib.empty(1), [None] * 100, calls=1000, repeats=repeats)
     res["empty_launch_us"] = us
     return res

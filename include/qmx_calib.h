@@ -37,6 +37,13 @@ int qmxc_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream
  * round either way; writes blocks*256 floats to `out`. */
 int qmxc_mfma(float* out, int iters, int blocks, int shape, void* stream);
 
+/* Co-issue of the matrix core and the vector ALU: `blocks` work-groups of 4
+ * waves, each wave issuing `iters` rounds of four independent
+ * v_mfma_f32_32x32x16_bf16, each followed by `fmas` independent float32 FMAs
+ * (with_mfma != 0), or the same FMAs alone (with_mfma == 0).  fmas is one of
+ * 0, 2, 4, 6, 8, 10, 12, 16 (else -1).  Writes blocks*256 floats to `out`. */
+int qmxc_mfma_valu(float* out, int iters, int blocks, int fmas, int with_mfma, void* stream);
+
 /* `blocks` work-groups of one wave that do nothing (the launch floor). */
 int qmxc_empty(int blocks, void* stream);
 

@@ -18,8 +18,10 @@ EXPORTS = {
                                  ctypes.c_void_p]),
     "qmxc_copy": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]),
     "qmxc_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "qmxc_mfma_valu": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]),
     "qmxc_empty": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p]),
 }
+MFMA_VALU_FMAS = (0, 2, 4, 6, 8, 10, 12, 16)
 FLOPS_PER_WAVE_ROUND = 8 * 2 * 16 * 16 * 32   # = 4 * 2 * 32 * 32 * 16
 
 _lib = None
@@ -66,6 +68,13 @@ def mfma(out: torch.Tensor, iters: int, blocks: int, shape: int = 32) -> None:
 
 def mfma_flops(iters: int, blocks: int) -> int:
     return blocks * 4 * iters * FLOPS_PER_WAVE_ROUND
+
+
+def mfma_valu(out: torch.Tensor, iters: int, blocks: int, fmas: int, with_mfma: bool = True) -> None:
+    """``blocks`` x 4 waves, each issuing ``iters`` rounds of four independent
+    32x32x16 bf16 MFMAs, each followed by ``fmas`` independent float32 FMAs (or
+    the FMAs alone); writes blocks*256 floats."""
+    _check(lib().qmxc_mfma_valu(out.data_ptr(), iters, blocks, fmas, int(with_mfma), _stream()), "qmxc_mfma_valu")
 
 
 def empty(blocks: int = 1) -> None:

@@ -92,6 +92,74 @@ __global__ __launch_bounds__(256) void mfma32_kernel(float* __restrict__ out, in
     out[(size_t)blockIdx.x * 256 + l] = s;
 }
 
+// Co-issue of the matrix core and the vector ALU: four independent chains of
+// v_mfma_f32_32x32x16_bf16, each instruction followed by F independent
+// v_fmac_f32 (16 chains, an SGPR multiplier, no literal), `iters` rounds.
+template <int F>
+__global__ __launch_bounds__(256) void mfma_valu_kernel(float* __restrict__ out, int iters, float m) {
+    const uint32_t l = threadIdx.x;
+    u32x4 ai = {0x3f803f80u ^ (l & 1u), 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ai);
+    f32x16 c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[j][e] = 0.f;
+    float f[16], g[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        f[j] = (float)(l + j) * 1e-3f;
+        g[j] = (float)(l ^ j) * 1e-4f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c[q], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < F; ++j) f[(q * F + j) % 16] = fmaf(m, g[(q * F + j) % 16], f[(q * F + j) % 16]);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += c[j][e];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += f[j];
+    out[(size_t)blockIdx.x * 256 + l] = s;
+}
+
+// The same F float FMAs per round without the matrix instructions.
+template <int F>
+__global__ __launch_bounds__(256) void valu_kernel(float* __restrict__ out, int iters, float m) {
+    const uint32_t l = threadIdx.x;
+    float f[16], g[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        f[j] = (float)(l + j) * 1e-3f;
+        g[j] = (float)(l ^ j) * 1e-4f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < F; ++j) f[(q * F + j) % 16] = fmaf(m, g[(q * F + j) % 16], f[(q * F + j) % 16]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += f[j];
+    out[(size_t)blockIdx.x * 256 + l] = s;
+}
+
+template <int F>
+int mfma_valu_go(float* out, int iters, int blocks, int with_mfma, hipStream_t st) {
+    if (with_mfma)
+        hipLaunchKernelGGL(mfma_valu_kernel<F>, dim3(blocks), dim3(256), 0, st, out, iters, 0.999f);
+    else
+        hipLaunchKernelGGL(valu_kernel<F>, dim3(blocks), dim3(256), 0, st, out, iters, 0.999f);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 __global__ void empty_kernel() {}
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -1; }
@@ -123,6 +191,22 @@ int qmxc_mfma(float* out, int iters, int blocks, int shape, void* stream) {
     else
         hipLaunchKernelGGL(mfma32_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), out, iters);
     return status(hipGetLastError());
+}
+
+int qmxc_mfma_valu(float* out, int iters, int blocks, int fmas, int with_mfma, void* stream) {
+    if (!out || iters < 0 || blocks <= 0) return -1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (fmas) {
+        case 0: return mfma_valu_go<0>(out, iters, blocks, with_mfma, st);
+        case 2: return mfma_valu_go<2>(out, iters, blocks, with_mfma, st);
+        case 4: return mfma_valu_go<4>(out, iters, blocks, with_mfma, st);
+        case 6: return mfma_valu_go<6>(out, iters, blocks, with_mfma, st);
+        case 8: return mfma_valu_go<8>(out, iters, blocks, with_mfma, st);
+        case 10: return mfma_valu_go<10>(out, iters, blocks, with_mfma, st);
+        case 12: return mfma_valu_go<12>(out, iters, blocks, with_mfma, st);
+        case 16: return mfma_valu_go<16>(out, iters, blocks, with_mfma, st);
+        default: return -1;
+    }
 }
 
 int qmxc_empty(int blocks, void* stream) {

@@ -118,6 +118,30 @@ def kernel_stats_markdown(stats_csv: str, substring: str = "qmx::") -> str:
     return "\n".join(out) + "\n"
 
 
+def counters_markdown(run_dirs, substring: str, exclude: str = "") -> str:
+    """Median per dispatch of every counter found in the counter_collection.csv
+    files under `run_dirs` (one rocprofv3 --pmc pass each), for the dispatches
+    whose kernel name holds `substring` (and not `exclude`), as markdown."""
+    vals, names = {}, set()
+    for d in run_dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as f:
+                for row in csv.DictReader(f):
+                    k = row["Kernel_Name"]
+                    if substring not in k or (exclude and exclude in k):
+                        continue
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                    names.add(k.split("(")[0].replace("void ", ""))
+    if not vals:
+        raise SystemExit(f"no counters for '{substring}' under {run_dirs}")
+    out = ["kernels: " + ", ".join(f"`{n}`" for n in sorted(names)), "",
+           "| counter | median per dispatch | dispatches |", "|---|---:|---:|"]
+    for name in sorted(vals):
+        v = vals[name]
+        out.append(f"| `{name}` | {statistics.median(v):.6g} | {len(v)} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -134,9 +158,16 @@ def main(argv=None) -> int:
     s.add_argument("--out", required=True)
     t = sub.add_parser("stats", help="markdown table of the library kernels in a --stats run")
     t.add_argument("csv", help="run_kernel_stats.csv")
+    k = sub.add_parser("counters", help="median per dispatch of the counters of several --pmc passes")
+    k.add_argument("dirs", nargs="+", help="one rocprofv3 output directory per pass")
+    k.add_argument("--kernel", required=True, help="substring of the kernel name to keep")
+    k.add_argument("--exclude", default="", help="substring of kernel names to drop")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(kernel_stats_markdown(args.csv), end="")
+        return 0
+    if args.cmd == "counters":
+        print(counters_markdown(args.dirs, args.kernel, args.exclude), end="")
         return 0
     if args.cmd == "copy":
         run_copy(args.mib, args.reps)

@@ -170,7 +170,8 @@ def test_qmm_config3_policy(orc, KNM):
     check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=qi.seed_for(3, M), cols=cols, reruns=1)
 
 
-@pytest.mark.parametrize("KNM", [(2048, 2048, 22), (10752, 2048, 85), (17408, 5120, 56)])
+@pytest.mark.parametrize("KNM", [(2048, 2048, 22), (4096, 4096, 16), (10752, 2048, 85), (14336, 4096, 33),
+                                 (17408, 5120, 56)])
 @pytest.mark.parametrize("route", ["qmm_t", "s2", "s3", "s4"])
 def test_qmm_config3_every_route(orc, KNM, route):
     K, N, M = KNM
