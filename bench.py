@@ -112,6 +112,13 @@ WORKLOADS = {
     # qmx_qmm_gather_sorted), illustrative shapes as above
     "gather_4bit_gs64_bf16": [affine("gather", 1, 2048, 4096, B=16, E=8), affine("gather", 16, 2048, 4096, B=16, E=8),
                               affine("gather", 1, 2048, 4096, B=16, E=8, sorted_idx=True)],
+    # M = 2..7 on the vector route, the matrix routes unsplit and split 2/4/8, and the policy's pick
+    "route_small_m_4bit_gs64_bf16": [c for n, k in ((4096, 4096), (14336, 5120), (5120, 5120), (27648, 5120),
+                                                    (4096, 14336))
+                                     for m in (2, 4, 5, 7)
+                                     for c in [affine("qmm", m, n, k), affine("qmv", m, n, k), affine("qmm_t", m, n, k)]
+                                     + [affine("splitk", m, n, k, splits=s) for s in (2, 4, 8)
+                                        if k // 256 >= s and (n + 127) // 128 * s <= 512]],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
     "q8_i8_14336x5120": [block("q8_i8", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
