@@ -50,15 +50,26 @@
 
 namespace qmx {
 
-template <int DT, int BITS, int GS, int MT, bool SBV>
+// WK: groups of waves along K.  Each of the 8 waves takes two k-steps (64
+// columns) of every K block, so a block is KB = 64 * WK columns, and the
+// 8 / WK waves of one group own NB fragments of 16 columns each: WK = 2 is the
+// 128-column tile, WK = 8 a 32-column tile for narrow problems (more
+// work-groups from few columns, every K group summed in the work-group).
+template <int DT, int BITS, int GS, int MT, bool SBV, int WK = 2>
 struct QmmCfg {
     static constexpr int BM = 16 * MT;
-    static constexpr int GPB = QMM_KB / GS;                   // groups per K block
+    static constexpr int WN = 8 / WK;                         // waves along N
+    static constexpr int BN = WN * QMM_NB * 16;               // columns per tile
+    static constexpr int KB = 64 * WK;                        // columns per K block
+    static constexpr int GPB = KB / GS;                       // groups per K block
     static constexpr int KS = GS / 32;                        // MFMA k-steps per group
-    // x: each wave-wide 16-byte copy fills 1 KB = 4 rows of 128 16-bit values.
-    static constexpr int XPT = (BM + 31) / 32;                // x copies per thread per block
-    static constexpr int XROWS = 32 * XPT;
-    static constexpr int X_BYTES = XROWS * 256;
+    // x: rows of KB 16-bit values (XRB bytes); each wave-wide 16-byte copy fills
+    // 1 KB = XRPC rows.
+    static constexpr int XRB = 2 * KB;
+    static constexpr int XRPC = 1024 / XRB;
+    static constexpr int XPT = (BM + 8 * XRPC - 1) / (8 * XRPC);   // x copies per thread per block
+    static constexpr int XROWS = 8 * XRPC * XPT;
+    static constexpr int X_BYTES = XROWS * XRB;
     // W: 16*BITS bytes per row per block.  1- and 2-bit rows are copied 4
     // bytes per lane (one and two copies per thread), the others 16 bytes per
     // lane.  For 3, 5 and 6 bits (fields may straddle words) the 128*BITS
@@ -68,15 +79,16 @@ struct QmmCfg {
     static constexpr bool ODD = !(BITS == 2 || BITS == 4 || BITS == 8);
     static constexpr bool W4B = BITS == 1 || BITS == 2;       // 4-byte W copies
     static constexpr bool WREP = ODD && !W4B;                 // 16-byte copies with repeats
-    static constexpr int W_ROW = 16 * BITS;
-    static constexpr int W_BYTES = QMM_BN * W_ROW;
+    static constexpr int W_ROW = KB * BITS / 8;
+    static constexpr int W_BYTES = BN * W_ROW;
+    static constexpr int W4_PPR = W_ROW / 16;                 // 16-byte pieces per row (4-bit codes)
     static constexpr int W_PIECES = W_BYTES / 16;
     static constexpr int WPT = W4B ? W_BYTES / (4 * QMM_THREADS)
                              : WREP ? (W_PIECES + QMM_THREADS - 1) / QMM_THREADS : W_BYTES / (16 * QMM_THREADS);
     // Scales then biases.  Staged per block, one 16-bit value per lane
     // (zero-extended to 4 bytes in LDS), unless SBV: then the work-group's whole
     // K range of both is copied once, before the ring, in 16-byte chunks.
-    static constexpr int SB_VALUES = 2 * QMM_BN * GPB;
+    static constexpr int SB_VALUES = 2 * BN * GPB;
     static constexpr int SBPT = SBV ? 0 : (SB_VALUES + QMM_THREADS - 1) / QMM_THREADS;
     static constexpr int SB_BYTES = SBPT * QMM_THREADS * 4;
     static constexpr int STAGE = X_BYTES + W_BYTES + SB_BYTES;
@@ -85,15 +97,17 @@ struct QmmCfg {
     static constexpr int NS = RING_LDS / STAGE < 4 ? RING_LDS / STAGE : 4;
     static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
     // SBV: 16-byte chunks (8 groups) per (scale/bias, column) held in LDS
-    static constexpr int SBV_CHUNKS = SBV ? ((160 * 1024 - NS * STAGE) / (2 * QMM_BN * 16) > 15
-                                                 ? 15 : (160 * 1024 - NS * STAGE) / (2 * QMM_BN * 16))
+    static constexpr int SBV_CHUNKS = SBV ? ((160 * 1024 - NS * STAGE) / (2 * BN * 16) > 15
+                                                 ? 15 : (160 * 1024 - NS * STAGE) / (2 * BN * 16))
                                           : 0;
-    static constexpr int SBV_BYTES = SBV_CHUNKS * 2 * QMM_BN * 16;
+    static constexpr int SBV_BYTES = SBV_CHUNKS * 2 * BN * 16;
     static constexpr bool CVT8 = DT == DT_BF16 && BITS == 8;  // 128 + q is not exact in bf16
     // Offset the expanded bf16 codes carry: 128 + q (q < 128); 8-bit bf16 codes are
     // converted instead, and f16 codes have their 1024 removed exactly before the MFMA.
     static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
-    static constexpr int RED_BYTES = QMM_WAVES_N * MT * QMM_NB * 4 * 64 * 4;
+    static constexpr int RED_FLOATS = WN * MT * QMM_NB * 4 * 64;   // one K group's tiles
+    static constexpr int RED_BYTES = (WK - 1) * RED_FLOATS * 4;
+    static_assert(WK == 2 || (WK == 8 && BITS == 4), "narrow tiles take 4-bit codes");
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
@@ -104,10 +118,17 @@ struct QmmCfg {
 };
 
 // Largest chunk count the staged scale/bias copy of one work-group may need.
-template <int DT, int BITS, int GS, int MT>
-constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true>::SBV_CHUNKS; }
+template <int DT, int BITS, int GS, int MT, int WK = 2>
+constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true, WK>::SBV_CHUNKS; }
 
-// 8-value chunk of the 128-column block that lane group g feeds at k-step s.
+// Bank spread of 4-bit W rows: piece p of row R is stored at slot p ^ w4_swz(R).
+template <int PPR>
+__device__ __forceinline__ int w4_swz(int R) {
+    if constexpr (PPR == 4) return (R >> 2) & 3;
+    else return R & (PPR - 1);
+}
+
+// 8-value chunk of the K block that lane group g feeds at k-step s.
 // Each step's 32 values lie inside one group of GS.  2-bit codes with GS >= 64
 // pair steps so that a lane's two steps are the two halves of one W word.
 template <int BITS, int GS>
@@ -248,12 +269,12 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
     const void* __restrict__ x, void* __restrict__ out, float* __restrict__ ws, QmxStrides sd,
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
-    using C = QmmCfg<DT, BITS, GS, MT, SBV>;
+    using C = QmmCfg<DT, BITS, GS, MT, SBV, WK>;
     // problem blockIdx.y of the batch (16-bit x, scales, biases and out)
     const long long bz = blockIdx.y, wz = qmx_w_matrix(sd, bz), xz = qmx_x_matrix(sd, bz);
     w += wz * sd.w;
@@ -274,8 +295,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const int rest = L / ntiles;
     const int mtile = rest % mtiles;
     const int split = rest / mtiles;
-    const int n0 = ntile * QMM_BN, m0 = mtile * C::BM;
-    const int nkb = K / QMM_KB;
+    const int n0 = ntile * C::BN, m0 = mtile * C::BM;
+    const int nkb = K / C::KB;
     const int kb0 = (int)((long)split * nkb / splits);
     const int kb1 = (int)((long)(split + 1) * nkb / splits);
     const int nk = kb1 - kb0;
@@ -284,18 +305,18 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & (QMM_WAVES_N - 1);   // column slice of this wave
-    const int wk = wave / QMM_WAVES_N;          // k-step pair of this wave: steps 2wk, 2wk+1 of each block
+    const int wn = wave & (C::WN - 1);   // column slice of this wave
+    const int wk = wave / C::WN;          // k-step pair of this wave: steps 2wk, 2wk+1 of each block
     const int lrow = lane & 15, lgrp = lane >> 4;
 
     // ---- per-thread sources of the stage copies at block 0 (block kb adds a fixed stride)
-    // x: copy i of this thread fills row r = 4*(8i + wave) + lane/16 of the stage at
-    // 16-byte slot lane%16, with chunk slot ^ (r & 15) of that row of x.
+    // x: copy i of this thread fills row r = XRPC*(8i + wave) + lane/(64/XRPC) of the
+    // stage at 16-byte slot lane%(64/XRPC), with chunk slot ^ (r & 15) of that row of x.
     const uint16_t* xsrc[C::XPT];
 #pragma unroll
     for (int i = 0; i < C::XPT; ++i) {
-        const int r = 4 * (8 * i + wave) + (lane >> 4);
-        const int c = (lane & 15) ^ (r & 15);
+        const int r = C::XRPC * (8 * i + wave) + lane / (64 / C::XRPC);
+        const int c = (lane % (64 / C::XRPC)) ^ (r & 15);
         xsrc[i] = static_cast<const uint16_t*>(x) + min(m0 + r, M - 1) * XR + 8 * c;
     }
     // W: tile rows R in 16-byte chunks (4-byte words for 2-bit codes); the chunk a
@@ -315,8 +336,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             R = v / BITS;
             q = 4 * (v % BITS);
         } else if constexpr (BITS == 4) {
-            R = 16 * wave + (lane >> 2);
-            q = 4 * ((lane & 3) ^ ((R >> 2) & 3));
+            R = (64 / C::W4_PPR) * wave + lane / C::W4_PPR;
+            q = 4 * ((lane % C::W4_PPR) ^ w4_swz<C::W4_PPR>(R));
         } else if constexpr (BITS == 8) {
             R = 8 * (8 * j + wave) + (lane >> 3);
             q = 4 * ((lane & 7) ^ ((R >> 1) & 7));
@@ -345,8 +366,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
     for (int j = 0; j < C::SBPT; ++j) {
         const int v = (QMM_THREADS * j + tid) % C::SB_VALUES;
-        const int which = v / (QMM_BN * C::GPB);
-        const int rem = v % (QMM_BN * C::GPB);
+        const int which = v / (C::BN * C::GPB);
+        const int rem = v % (C::BN * C::GPB);
         const int col = rem / C::GPB, g = rem % C::GPB;
         sbsrc[j] = static_cast<const uint16_t*>(which ? biases : scales) + (size_t)min(n0 + col, N - 1) * G + g;
     }
@@ -356,7 +377,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         unsigned char* Wl = X + C::X_BYTES;
         unsigned char* SB = Wl + C::W_BYTES;
 #pragma unroll
-        for (int i = 0; i < C::XPT; ++i) dma<16>(xsrc[i] + (size_t)kb * QMM_KB, X + (8 * i + wave) * 1024);
+        for (int i = 0; i < C::XPT; ++i) dma<16>(xsrc[i] + (size_t)kb * C::KB, X + (8 * i + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < C::WPT; ++j) {
             if constexpr (C::W4B)
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
                         bf[st][nf] = expand_stream<DT, BITS>(rw[o >> 2], BITS > 1 ? rw[(o >> 2) + 1] : 0u, o & 3);
                     } else if constexpr (BITS == 4) {
                         const uint32_t word = *reinterpret_cast<const uint32_t*>(
-                            Wl + R * C::W_ROW + (((c >> 2) ^ ((R >> 2) & 3)) << 4) + 4 * (c & 3));
+                            Wl + R * C::W_ROW + (((c >> 2) ^ w4_swz<C::W4_PPR>(R)) << 4) + 4 * (c & 3));
                         bf[st][nf] = expand4<DT>(word);
                     } else if constexpr (BITS == 8) {
                         const u32x2 wv = *reinterpret_cast<const u32x2*>(
@@ -437,10 +458,10 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
                     const int ga = kb * C::GPB + g;                   // group index within the row
                     const int at = (col * sb_nch + (ga >> 3) - sb_c0) * 8 + (ga & 7);
                     sr = SBVl[at];
-                    br = SBVl[QMM_BN * sb_nch * 8 + at];
+                    br = SBVl[C::BN * sb_nch * 8 + at];
                 } else {
                     sr = SB[col * C::GPB + g];
-                    br = SB[QMM_BN * C::GPB + col * C::GPB + g];
+                    br = SB[C::BN * C::GPB + col * C::GPB + g];
                 }
                 const float s = DT == DT_F16 ? f16_bits_to_f32(sr) : bf16_bits_to_f32(sr);
                 const float b = DT == DT_F16 ? f16_bits_to_f32(br) : bf16_bits_to_f32(br);
@@ -458,8 +479,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
             for (int mf = 0; mf < MT; ++mf) {
                 const int r = mf * 16 + lrow;
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c0 ^ (r & 15)) << 4));
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c1 ^ (r & 15)) << 4));
+                const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * C::XRB + ((c0 ^ (r & 15)) << 4));
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * C::XRB + ((c1 ^ (r & 15)) << 4));
 #pragma unroll
                 for (int nf = 0; nf < NB; ++nf) {
                     gacc[mf][nf] = mfma16x16x32<DT>(a0, bf[0][nf], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -482,8 +503,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
 #pragma unroll
         for (int mf = 0; mf < MT; ++mf) {
             const int r = mf * 16 + lrow;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c0 ^ (r & 15)) << 4));
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * 256 + ((c1 ^ (r & 15)) << 4));
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(X + r * C::XRB + ((c0 ^ (r & 15)) << 4));
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(X + r * C::XRB + ((c1 ^ (r & 15)) << 4));
 #pragma unroll
             for (int gp = 0; gp < NG; ++gp) {
                 f32x4 gacc[NB];
@@ -510,13 +531,13 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         // one copy per (scale/bias, column, chunk), lane v at LDS slot v; issued before
         // the ring so that the first stage's wait also covers them (copies of a wave
         // complete in order)
-        const int lanes = 2 * QMM_BN * sb_nch;
+        const int lanes = 2 * C::BN * sb_nch;
         unsigned char* base = smem + NS * C::STAGE;
         for (int j = 0; j * QMM_THREADS < lanes; ++j) {
             const int v = QMM_THREADS * j + tid;
             if (v < lanes) {
-                const int which = v / (QMM_BN * sb_nch);
-                const int rem = v - which * (QMM_BN * sb_nch);
+                const int which = v / (C::BN * sb_nch);
+                const int rem = v - which * (C::BN * sb_nch);
                 const int col = rem / sb_nch, ch = rem - col * sb_nch;
                 const uint16_t* src = static_cast<const uint16_t*>(which ? biases : scales) +
                                       (size_t)min(n0 + col, N - 1) * G + 8 * (sb_c0 + min(ch, sb_last));
@@ -544,29 +565,33 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     }
     stage_barrier<0>();
 
-    // add the second half's tiles to the first half's, then store
+    // add the other K groups' tiles to the first group's, in ascending group
+    // order, then store
     float* red = reinterpret_cast<float*>(smem);
-    if (wk == 1) {
+    if (wk > 0) {
 #pragma unroll
         for (int mf = 0; mf < MT; ++mf)
 #pragma unroll
             for (int nf = 0; nf < NB; ++nf)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane] = run[mf][nf][v];
+                    red[(wk - 1) * C::RED_FLOATS + (((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane] = run[mf][nf][v];
     }
     stage_barrier<0>();
-    if (wk == 1) return;
+    if (wk > 0) return;
     // every partner value is read before the first store, so the LDS reads share
     // one wait instead of one each in front of every (row-predicated) store
 #pragma unroll
-    for (int mf = 0; mf < MT; ++mf)
+    for (int g = 1; g < WK; ++g)
 #pragma unroll
-        for (int nf = 0; nf < NB; ++nf)
+        for (int mf = 0; mf < MT; ++mf)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) run[mf][nf][v] += red[(((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane];
+            for (int nf = 0; nf < NB; ++nf)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    run[mf][nf][v] += red[(g - 1) * C::RED_FLOATS + (((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane];
     const int nl = n0 + wn * (NB * 16) + lrow;   // this lane's column in fragment 0
-    const bool cols_ok = n0 + QMM_BN <= N;
+    const bool cols_ok = n0 + C::BN <= N;
 #pragma unroll
     for (int mf = 0; mf < MT; ++mf)
 #pragma unroll
@@ -588,33 +613,34 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         }
 }
 
-template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV>
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK>
 void qmm_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out, float* ws,
             QmxStrides sd, int M, int N, int K, int splits, int ntiles, int mtiles, int total, int per_xcd,
             hipStream_t st) {
-    hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV>), grid, dim3(QMM_THREADS), 0, st, w, s, b, x,
-                       out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd);
+    hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV, WK>), grid, dim3(QMM_THREADS), 0, st, w, s, b,
+                       x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd);
 }
 
-template <int DT, int BITS, int GS, int MT>
+template <int DT, int BITS, int GS, int MT, int WK = 2>
 hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, int mtiles,
                          hipStream_t st) {
-    const int ntiles = (N + QMM_BN - 1) / QMM_BN;
+    using C = QmmCfg<DT, BITS, GS, MT, false, WK>;
+    const int ntiles = (N + C::BN - 1) / C::BN;
     const int total = ntiles * mtiles * splits;
     const int per_xcd = (total + 7) / 8;
     const dim3 grid(8 * per_xcd, batch);
     // Staged scales/biases need 16-byte aligned arrays, rows of whole 16-byte chunks
     // (K/GS a multiple of 8) and a K range whose chunks (plus one for alignment and
     // one for an odd count) fit the LDS left over.
-    const int G = K / GS, nkb = K / QMM_KB;
+    const int G = K / GS, nkb = K / C::KB;
     const int nk_max = (nkb + splits - 1) / splits;
     const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
                          (sd.sb * 2) % 16 == 0;
     const bool sbv = aligned && K > 0 && G % 8 == 0 &&
-                     (nk_max * (QMM_KB / GS) + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT>();
+                     (nk_max * C::GPB + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT, WK>();
 #define QMM_GO(SPLIT_, SBV_) \
-    qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
+    qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_, WK>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
     if (splits > 1) {
         if (sbv) QMM_GO(true, true);
         else QMM_GO(true, false);
@@ -629,6 +655,13 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
 template <int DT, int BITS, int GS>
 hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
+    if constexpr (BITS == 4) {
+        // narrow tiles: one tile of 16 or 32 rows
+        if (qmm_narrow(M, N, K, BITS, batch, splits, device_cu_count())) {
+            if (M <= 16) return qmm_launch_mt<DT, BITS, GS, 1, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
+            return qmm_launch_mt<DT, BITS, GS, 2, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
+        }
+    }
     const int mt = qmm_mtiles_for(M, (long long)((N + QMM_BN - 1) / QMM_BN) * batch, device_cu_count(), K);
 #define QMM_MT(MT_) qmm_launch_mt<DT, BITS, GS, MT_>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, mt, st)
     switch (qmm_mt_for(M, mt)) {

@@ -94,21 +94,20 @@ int device_cus() {
     return cus;
 }
 
-// Below M = 8 qmv reads each weight once for up to 4 rows of x, but its vector
-// work grows with M: about 1.125 + 0.5 * m instructions per code for a pass
-// over m <= 4 rows (code expansion plus one dot2 per pair and row), and a
-// second pass for M > 4.  The matrix route costs about its weight bytes at
-// 2.3 TB/s with a floor of about 9 us; qmv has a floor of about 5.5 us and
-// about 8.9e-8 us per code and instruction.  Measured on the chip at N x K =
-// 4096 x 4096 and 14336 x 5120 for M = 2..7: qmv stays ahead on the smaller
-// matrix up to M = 5, the matrix route from M = 4 on the larger one.
-bool small_m_prefers_matrix(int M, int N, int K, int bits, int batch) {
+// Below M = 8 qmv reads each weight once for up to 4 rows of x, and makes a
+// second pass for M > 4; a pass costs the same for 3 and 4 rows.  Measured on
+// the chip (N x K from 2048 x 2048 to 14336 x 5120, M = 2..7, 4-bit gs 64):
+// about 2.5 us plus 0.16, 0.28 or 0.45 us per million codes for M = 2, 3..4
+// and 5..7.  Where 32-column tiles apply, the matrix route has one work-group
+// walk all of K: about 4.5 us plus 0.95 us per 1024 columns of K; otherwise
+// it costs about its weight bytes at 2.3 TB/s with a floor of about 9 us.
+bool small_m_prefers_matrix(int M, int N, int K, int bits, int batch, int cus) {
     if (M < 2 || M >= 8) return false;
-    const double codes = (double)N * K * (batch > 0 ? batch : 1);
-    const int first = M < 4 ? M : 4, second = M - first;
-    const double per_code = 1.125 + 0.5 * first + (second > 0 ? 1.125 + 0.5 * second : 0.0);
-    const double t_qmv = std::max(5.5, 8.9e-8 * codes * per_code);
-    const double t_mat = std::max(9.0, codes * bits / 8.0 / 2.3e6);
+    const double mcodes = (double)N * K * (batch > 0 ? batch : 1) / 1e6;
+    const double t_qmv = 2.5 + (M == 2 ? 0.16 : M <= 4 ? 0.28 : 0.45) * mcodes;
+    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, batch > 0 ? batch : 1, cus)
+                             ? 4.5 + 0.95 * K / 1024.0
+                             : std::max(9.0, mcodes * 1e6 * bits / 8.0 / 2.3e6);
     return t_mat < t_qmv;
 }
 
@@ -119,7 +118,7 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     if (num_cus <= 0) num_cus = kDefaultCUs;
     // float32, K that the staged kernel cannot block and M < 8 stay on qmv,
     // unless M is 2..7 and the vector-ALU work of qmv outweighs the matrix route.
-    if (dtype == QMX_F32 || K % QMM_KB != 0 || (M < 8 && !small_m_prefers_matrix(M, N, K, bits, batch))) {
+    if (dtype == QMX_F32 || K % QMM_KB != 0 || (M < 8 && !small_m_prefers_matrix(M, N, K, bits, batch, num_cus))) {
         if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
         *route = QMX_ROUTE_QMV;
         *splits = 1;
@@ -127,7 +126,8 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     }
     const long long col_tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
     const long long tiles = col_tiles * qmx::qmm_mtiles_for(M, col_tiles, num_cus, K);
-    const int s = qmx::qmm_policy_splits(tiles, K, num_cus);
+    int s = qmx::qmm_policy_splits(tiles, K, num_cus);
+    if (s >= 2 && qmx::qmm_narrow_preferred(M, N, K, bits, batch, num_cus)) s = 1;
     *route = s >= 2 ? QMX_ROUTE_QMM_T_SPLITK : QMX_ROUTE_QMM_T;
     *splits = s;
     return QMX_OK;

@@ -179,13 +179,17 @@ def test_block_validation():
 
 @pytest.mark.parametrize("M,N,K,dtype,route,splits", [
     (1, 4096, 4096, BF16, "qmv", 1),
-    (7, 4096, 4096, BF16, "qmv", 1),
+    (4, 4096, 4096, BF16, "qmv", 1),
+    (7, 4096, 4096, BF16, "qmm_t", 1),                # a second qmv pass costs more than 32-column tiles
     (16, 4096, 4096, F32, "qmv", 1),                 # float32 never takes the matrix cores
-    (16, 4096, 4096, BF16, "qmm_t_splitk", 8),       # 32 tiles on 256 CUs
+    (16, 4096, 4096, BF16, "qmm_t", 1),              # 128 32-column tiles instead of 32 x 8 partitions
+    (16, 4096, 4096, F16, "qmm_t", 1),
     (16, 4096, 256, BF16, "qmm_t", 1),               # K < 1024 stays unsplit
     (16, 4096, 768, BF16, "qmm_t", 1),
-    (16, 4096, 1024, BF16, "qmm_t_splitk", 4),       # capped at K / 256 partitions
-    (22, 2048, 2048, BF16, "qmm_t_splitk", 8),       # capped at K / 256 partitions
+    (16, 4096, 1024, BF16, "qmm_t", 1),              # 2 narrow blocks against 2 blocks + the accumulate
+    (22, 2048, 2048, BF16, "qmm_t", 1),              # 64 32-column tiles, 4 blocks each
+    (22, 2048, 8192, BF16, "qmm_t_splitk", 16),      # 16 narrow blocks: too long for one work-group
+    (40, 2048, 2048, BF16, "qmm_t_splitk", 8),       # M > 32 stays on 128-column tiles
     (85, 2048, 10752, BF16, "qmm_t_splitk", 8),       # 2 M tiles of 43 rows x 16 N tiles
     (128, 4096, 4096, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 N tiles
     (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
@@ -196,18 +200,29 @@ def test_block_validation():
     (257, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 128-row tiles: 3 x 32 split 2 = 192 groups (64-row: 160)
     (384, 4096, 4096, BF16, "qmm_t", 1),             # 64-row tiles: 6 x 32 = 192 groups, as many as 3 x 32 split 2
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
-    (8, 4096, 4096, F16, "qmm_t_splitk", 8),
+    (8, 4096, 4096, F16, "qmm_t", 1),
+    (16, 14336, 4096, BF16, "qmm_t_splitk", 2),      # 448 narrow tiles would not all be resident
     (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
     (2, 14336, 5120, BF16, "qmv", 1),                # M = 2..7: qmv while its vector work is small
     (4, 14336, 5120, BF16, "qmm_t_splitk", 2),       # ... the matrix route once it is not
     (7, 27648, 5120, BF16, "qmm_t", 1),
-    (5, 5120, 5120, F16, "qmm_t_splitk", 6),
-    (4, 5120, 5120, BF16, "qmv", 1),
+    (5, 5120, 5120, F16, "qmm_t", 1),
+    (4, 5120, 5120, BF16, "qmm_t", 1),               # measured: 32-column tiles 9.5 us, qmv 12.1 us
     (7, 2048, 2048, BF16, "qmv", 1),
     (7, 14336, 5120, F32, "qmv", 1),                 # float32 stays on qmv at every M
 ])
 def test_plan_table(M, N, K, dtype, route, splits):
     assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)
+
+
+def test_plan_narrow_tiles_take_4bit_codes_only():
+    """The 32-column tiles read 4-bit codes; other widths keep the 128-column
+    tiles and their split-K partitions (capped at K / 256)."""
+    for bits in (1, 2, 3, 5, 6, 8):
+        assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 8)
+        assert qmx.plan(16, 4096, 1024, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 4)
+    # K not a multiple of 512 keeps them too
+    assert qmx.plan(16, 4096, 1152, 4, 64, BF16, num_cus=256)[0] == "qmm_t_splitk"
 
 
 def test_plan_respects_split_limits():
@@ -220,9 +235,9 @@ def test_plan_respects_split_limits():
         qmx.plan(16, 4096, 96, 2, 32, F32, 256)      # qmv route cannot take 192-bit rows
     with pytest.raises(qmx.QmxError):
         qmx.plan(1, 4096, 4096, 7, 64, BF16, 256)      # 7-bit codes are not a supported width
-    for bits in (1, 3, 5, 6):                          # the other widths route like 4-bit
+    for bits in (1, 3, 5, 6):                          # the other widths route like 4-bit on 128-column tiles
         assert qmx.plan(1, 4096, 4096, bits, 64, BF16, 256) == ("qmv", 1)
-        assert qmx.plan(16, 4096, 4096, bits, 64, BF16, 256) == qmx.plan(16, 4096, 4096, 4, 64, BF16, 256)
+        assert qmx.plan(40, 4096, 4096, bits, 64, BF16, 256) == qmx.plan(40, 4096, 4096, 4, 64, BF16, 256)
 
 
 def test_binding_rejects_cpu_tensors():
@@ -259,13 +274,16 @@ def test_batched_validation():
 
 
 def test_batched_plan_counts_every_problem():
-    # one problem of (M=16, N=256, K=4096) has 2 tiles: 16 partitions; 8 of them: 16 tiles, 16 partitions;
+    # one problem of (M=40, N=256, K=4096) has 2 tiles: 16 partitions; 8 of them: 16 tiles, 16 partitions;
     # 200 of them fill the chip without a split
-    assert qmx.plan_batched(1, 16, 256, 4096, 4, 64, BF16, 256) == qmx.plan(16, 256, 4096, 4, 64, BF16, 256)
-    r8, s8 = qmx.plan_batched(8, 16, 256, 4096, 4, 64, BF16, 256)
-    r1, s1 = qmx.plan_batched(1, 16, 256, 4096, 4, 64, BF16, 256)
+    assert qmx.plan_batched(1, 40, 256, 4096, 4, 64, BF16, 256) == qmx.plan(40, 256, 4096, 4, 64, BF16, 256)
+    r8, s8 = qmx.plan_batched(8, 40, 256, 4096, 4, 64, BF16, 256)
+    r1, s1 = qmx.plan_batched(1, 40, 256, 4096, 4, 64, BF16, 256)
     assert r8 == r1 == "qmm_t_splitk" and s8 <= s1
-    assert qmx.plan_batched(200, 16, 256, 4096, 4, 64, BF16, 256) == ("qmm_t", 1)
+    assert qmx.plan_batched(200, 40, 256, 4096, 4, 64, BF16, 256) == ("qmm_t", 1)
+    # at M = 16 the 32-column tiles of 8 problems (64 of them) take the batch unsplit
+    assert qmx.plan_batched(1, 16, 256, 4096, 4, 64, BF16, 256)[0] == "qmm_t_splitk"
+    assert qmx.plan_batched(8, 16, 256, 4096, 4, 64, BF16, 256) == ("qmm_t", 1)
     assert qmx.plan_batched(8, 1, 4096, 4096, 4, 64, BF16, 256) == ("qmv", 1)
 
 

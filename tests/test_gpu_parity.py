@@ -139,11 +139,34 @@ def test_qmm_t_small_m_tails(orc, M):
     check_affine(orc, "qmm_t", M, 200, 512, 4, 64, qi.BF16, seed=1200 + M)
 
 
-@pytest.mark.parametrize("M,N,K", [(3, 14336, 5120), (7, 27648, 5120), (5, 5120, 5120)])
+@pytest.mark.parametrize("M,N,K", [(3, 14336, 5120), (7, 27648, 5120), (5, 5120, 5120), (3, 8192, 4096)])
 def test_small_m_matrix_route(orc, M, N, K):
     """M < 8 shapes that the policy sends to the matrix cores (sampled columns)."""
     assert qmx.plan(M, N, K, 4, 64, qi.BF16)[0] != "qmv"
     check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=1250 + M, cols=sample_cols(N, 256, M), reruns=1)
+
+
+# (M, N, K): 4-bit unsplit qmm_t with M <= 32 and few 128-column tiles runs on
+# 32-column tiles whose 8 waves split each 512-column K block: 16- and 32-row
+# tiles, ragged N, one to five blocks, K ranges whose scales and biases are
+# staged whole or per block (K / group size not a multiple of 8).
+NARROW_SHAPES = [(16, 1000, 1536), (32, 96, 2560), (9, 33, 512), (25, 4100, 1024), (1, 70, 1024)]
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
+def test_qmm_t_narrow_tiles(orc, gs, dt):
+    for i, (M, N, K) in enumerate(NARROW_SHAPES):
+        check_affine(orc, "qmm_t", M, N, K, 4, gs, dt, seed=1280 + 10 * i + gs + dt, reruns=1)
+
+
+def test_qmm_narrow_policy_shapes(orc):
+    """The shapes the policy sends unsplit to 32-column tiles (they would split K
+    on 128-column tiles): the config-3 M = 22 and M = 16 calls, and M = 8 of the
+    4096 x 4096 sweep, every output against the oracle."""
+    for M, N, K in ((22, 2048, 2048), (16, 4096, 4096), (8, 4096, 4096)):
+        assert qmx.plan(M, N, K, 4, 64, qi.BF16, num_cus=256) == ("qmm_t", 1)
+        check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=1290 + M, reruns=1)
 
 
 @pytest.mark.parametrize("bits", ALL_BITS)
@@ -445,6 +468,8 @@ def _strided(x, kind):
     (2, 20, 384, 1024, 4, 64, qi.BF16, True, "odd"),           # matrix cores, odd offset (copied first)
     (2, 16, 256, 4096, 4, 64, qi.BF16, False, "contiguous"),   # split-K across the batch
     (3, 85, 128, 2560, 5, 32, qi.BF16, False, "odd"),          # two M tiles, split-K, odd offset
+    (6, 16, 1024, 2048, 4, 64, qi.BF16, False, "padded"),      # 32-column tiles across the batch
+    (4, 25, 2048, 1024, 4, 128, qi.F16, True, "odd"),          # 32-column tiles, shared weights, x copied first
 ])
 def test_batched_strided_and_odd_offset(orc, B, M, N, K, bits, gs, dt, shared, layout):
     route = qmx.plan_batched(B, M, N, K, bits, gs, dt, 256)
@@ -482,6 +507,7 @@ def test_batched_single_problem_matches_unbatched(orc):
     (5, 160, 768, 3, 32, qi.F16, "odd"),             # qmv route, x copied first
     (24, 256, 2048, 4, 64, qi.BF16, "padded"),        # matrix cores
     (40, 128, 4096, 6, 128, qi.F16, "odd"),          # matrix cores, split-K, x copied first
+    (16, 512, 1024, 4, 64, qi.BF16, "padded"),       # matrix cores on 32-column tiles
 ])
 def test_gather_qmm(orc, M, N, K, bits, gs, dt, layout):
     """Problem i takes weight matrix w_index[i] and x matrix x_index[i] (repeated
