@@ -38,7 +38,8 @@ int qmm_mtiles_for(int M, long long col_tiles, int cus, int K) {
 }
 
 bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int cus) {
-    if (bits != 4 || K % 512 != 0 || M < 1 || M > 32 || splits != 1 || cus <= 0) return false;
+    if ((bits != 2 && bits != 4 && bits != 8) || K % 512 != 0 || M < 1 || M > 32 || splits != 1 || cus <= 0)
+        return false;
     // the 128-column tiles leave compute units idle
     return (long long)((N + QMM_BN - 1) / QMM_BN) * batch < cus;
 }
@@ -48,9 +49,12 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
 // the narrow call saves the accumulate kernel and its launch instead.  Measured
 // per call at M = 8..32, N = 1024..14336, K = 2048..8192 on 256 CUs: narrow is
 // up to 1.4x faster while it walks at most 4 blocks more than a partition,
-// even at 6, and 8-25% slower from 8 on at 32 rows.
-bool qmm_narrow_preferred(int M, int N, int K, int bits, long long batch, int cus) {
-    if (!qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
+// even at 6, and 8-25% slower from 8 on at 32 rows.  At gs 32 each wave
+// carries two group epilogues per block, and narrow tiles were 1-6% slower than
+// the split plan at M = 8, N = K = 4096 (2, 4 and 8 bits), so they are not
+// preferred there.
+bool qmm_narrow_preferred(int M, int N, int K, int bits, int gs, long long batch, int cus) {
+    if (gs < 64 || !qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
     const long long tiles = (long long)((N + 31) / 32) * batch;
     if (4 * tiles < cus || tiles > cus) return false;
     const long long wide = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;

@@ -81,7 +81,8 @@ struct QmmCfg {
     static constexpr bool WREP = ODD && !W4B;                 // 16-byte copies with repeats
     static constexpr int W_ROW = KB * BITS / 8;
     static constexpr int W_BYTES = BN * W_ROW;
-    static constexpr int W4_PPR = W_ROW / 16;                 // 16-byte pieces per row (4-bit codes)
+    // copy slots per W row: 4-byte words for 1- and 2-bit codes, else 16-byte pieces
+    static constexpr int W_SLOTS = W4B ? W_ROW / 4 : W_ROW / 16;
     static constexpr int W_PIECES = W_BYTES / 16;
     static constexpr int WPT = W4B ? W_BYTES / (4 * QMM_THREADS)
                              : WREP ? (W_PIECES + QMM_THREADS - 1) / QMM_THREADS : W_BYTES / (16 * QMM_THREADS);
@@ -107,7 +108,7 @@ struct QmmCfg {
     static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
     static constexpr int RED_FLOATS = WN * MT * QMM_NB * 4 * 64;   // one K group's tiles
     static constexpr int RED_BYTES = (WK - 1) * RED_FLOATS * 4;
-    static_assert(WK == 2 || (WK == 8 && BITS == 4), "narrow tiles take 4-bit codes");
+    static_assert(WK == 2 || (WK == 8 && (BITS == 2 || BITS == 4 || BITS == 8)), "narrow tiles: 2, 4, 8 bits");
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
@@ -121,11 +122,17 @@ struct QmmCfg {
 template <int DT, int BITS, int GS, int MT, int WK = 2>
 constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true, WK>::SBV_CHUNKS; }
 
-// Bank spread of 4-bit W rows: piece p of row R is stored at slot p ^ w4_swz(R).
-template <int PPR>
-__device__ __forceinline__ int w4_swz(int R) {
-    if constexpr (PPR == 4) return (R >> 2) & 3;
-    else return R & (PPR - 1);
+// Bank spread of 2-, 4- and 8-bit W rows of SLOTS copy slots: slot p of row R
+// holds piece (or word) p ^ w_swz(R) of the row.  The 128-column rows (4, 8 and
+// 8 slots) XOR a few row bits above the ones a wave's lanes share; the 512-column
+// rows (16 or 32 slots) the low 4 bits of the row, so the 16 rows of a fragment
+// read distinct slots.
+template <int BITS, int SLOTS>
+__device__ __forceinline__ int w_swz(int R) {
+    if constexpr (SLOTS >= 16) return R & 15;
+    else if constexpr (BITS == 4) return (R >> 2) & 3;
+    else if constexpr (BITS == 8) return (R >> 1) & 7;
+    else return (R >> 3) & 7;
 }
 
 // 8-value chunk of the K block that lane group g feeds at k-step s.
@@ -335,15 +342,13 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             const int v = (QMM_THREADS * j + tid) % C::W_PIECES;
             R = v / BITS;
             q = 4 * (v % BITS);
-        } else if constexpr (BITS == 4) {
-            R = (64 / C::W4_PPR) * wave + lane / C::W4_PPR;
-            q = 4 * ((lane % C::W4_PPR) ^ w4_swz<C::W4_PPR>(R));
-        } else if constexpr (BITS == 8) {
-            R = 8 * (8 * j + wave) + (lane >> 3);
-            q = 4 * ((lane & 7) ^ ((R >> 1) & 7));
         } else {
-            R = 8 * (8 * j + wave) + (lane >> 3);
-            q = (lane & 7) ^ ((R >> 3) & 7);
+            // 2, 4, 8 bits: copy j of the wave fills 64 / W_SLOTS whole rows, lane l
+            // slot l % W_SLOTS of its row, with the piece (or word) the slot holds
+            constexpr int SL = C::W_SLOTS;
+            R = (64 / SL) * (8 * j + wave) + lane / SL;
+            const int piece = (lane % SL) ^ w_swz<BITS, SL>(R);
+            q = C::W4B ? piece : 4 * piece;
         }
         wsrc[j] = w + (size_t)min(n0 + R, N - 1) * row_words + q;
     }
@@ -413,8 +418,8 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
             const int R = wn * (NB * 16) + nf * 16 + lrow;
             if constexpr (BITS == 2 && GS >= 64) {
                 const int c = kchunk<BITS, GS>(2 * wk, lgrp);   // both steps share word c / 2
-                const uint32_t word = *reinterpret_cast<const uint32_t*>(Wl + R * C::W_ROW +
-                                                                         (((c >> 1) ^ ((R >> 3) & 7)) << 2));
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(
+                    Wl + R * C::W_ROW + (((c >> 1) ^ w_swz<BITS, C::W_SLOTS>(R)) << 2));
                 bf[0][nf] = expand2<DT>(word & 0xffffu);
                 bf[1][nf] = expand2<DT>(word >> 16);
             } else {
@@ -430,15 +435,15 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
                         bf[st][nf] = expand_stream<DT, BITS>(rw[o >> 2], BITS > 1 ? rw[(o >> 2) + 1] : 0u, o & 3);
                     } else if constexpr (BITS == 4) {
                         const uint32_t word = *reinterpret_cast<const uint32_t*>(
-                            Wl + R * C::W_ROW + (((c >> 2) ^ w4_swz<C::W4_PPR>(R)) << 4) + 4 * (c & 3));
+                            Wl + R * C::W_ROW + (((c >> 2) ^ w_swz<BITS, C::W_SLOTS>(R)) << 4) + 4 * (c & 3));
                         bf[st][nf] = expand4<DT>(word);
                     } else if constexpr (BITS == 8) {
                         const u32x2 wv = *reinterpret_cast<const u32x2*>(
-                            Wl + R * C::W_ROW + (((c >> 1) ^ ((R >> 1) & 7)) << 4) + 8 * (c & 1));
+                            Wl + R * C::W_ROW + (((c >> 1) ^ w_swz<BITS, C::W_SLOTS>(R)) << 4) + 8 * (c & 1));
                         bf[st][nf] = expand8<DT>(wv.x, wv.y);
                     } else {
-                        const uint32_t word = *reinterpret_cast<const uint32_t*>(Wl + R * C::W_ROW +
-                                                                                 (((c >> 1) ^ ((R >> 3) & 7)) << 2));
+                        const uint32_t word = *reinterpret_cast<const uint32_t*>(
+                            Wl + R * C::W_ROW + (((c >> 1) ^ w_swz<BITS, C::W_SLOTS>(R)) << 2));
                         bf[st][nf] = expand2<DT>((word >> (16 * (c & 1))) & 0xffffu);
                     }
                 }
@@ -641,13 +646,16 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
                      (nk_max * C::GPB + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT, WK>();
 #define QMM_GO(SPLIT_, SBV_) \
     qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_, WK>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
-    if (splits > 1) {
-        if (sbv) QMM_GO(true, true);
-        else QMM_GO(true, false);
-    } else {
-        if (sbv) QMM_GO(false, true);
-        else QMM_GO(false, false);
+    if constexpr (WK == 2) {
+        if (splits > 1) {
+            if (sbv) QMM_GO(true, true);
+            else QMM_GO(true, false);
+            return hipGetLastError();
+        }
     }
+    // narrow tiles run unsplit only
+    if (sbv) QMM_GO(false, true);
+    else QMM_GO(false, false);
 #undef QMM_GO
     return hipGetLastError();
 }
@@ -655,7 +663,7 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
 template <int DT, int BITS, int GS>
 hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, hipStream_t st) {
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
         // narrow tiles: one tile of 16 or 32 rows
         if (qmm_narrow(M, N, K, BITS, batch, splits, device_cu_count())) {
             if (M <= 16) return qmm_launch_mt<DT, BITS, GS, 1, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);

@@ -101,11 +101,11 @@ int device_cus() {
 // and 5..7.  Where 32-column tiles apply, the matrix route has one work-group
 // walk all of K: about 4.5 us plus 0.95 us per 1024 columns of K; otherwise
 // it costs about its weight bytes at 2.3 TB/s with a floor of about 9 us.
-bool small_m_prefers_matrix(int M, int N, int K, int bits, int batch, int cus) {
+bool small_m_prefers_matrix(int M, int N, int K, int bits, int gs, int batch, int cus) {
     if (M < 2 || M >= 8) return false;
     const double mcodes = (double)N * K * (batch > 0 ? batch : 1) / 1e6;
     const double t_qmv = 2.5 + (M == 2 ? 0.16 : M <= 4 ? 0.28 : 0.45) * mcodes;
-    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, batch > 0 ? batch : 1, cus)
+    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, gs, batch > 0 ? batch : 1, cus)
                              ? 4.5 + 0.95 * K / 1024.0
                              : std::max(9.0, mcodes * 1e6 * bits / 8.0 / 2.3e6);
     return t_mat < t_qmv;
@@ -118,7 +118,7 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     if (num_cus <= 0) num_cus = kDefaultCUs;
     // float32, K that the staged kernel cannot block and M < 8 stay on qmv,
     // unless M is 2..7 and the vector-ALU work of qmv outweighs the matrix route.
-    if (dtype == QMX_F32 || K % QMM_KB != 0 || (M < 8 && !small_m_prefers_matrix(M, N, K, bits, batch, num_cus))) {
+    if (dtype == QMX_F32 || K % QMM_KB != 0 || (M < 8 && !small_m_prefers_matrix(M, N, K, bits, gs, batch, num_cus))) {
         if (K % qmx::qmv_chunk_codes(bits) != 0) return QMX_ERR_SHAPE;
         *route = QMX_ROUTE_QMV;
         *splits = 1;
@@ -127,7 +127,7 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     const long long col_tiles = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
     const long long tiles = col_tiles * qmx::qmm_mtiles_for(M, col_tiles, num_cus, K);
     int s = qmx::qmm_policy_splits(tiles, K, num_cus);
-    if (s >= 2 && qmx::qmm_narrow_preferred(M, N, K, bits, batch, num_cus)) s = 1;
+    if (s >= 2 && qmx::qmm_narrow_preferred(M, N, K, bits, gs, batch, num_cus)) s = 1;
     *route = s >= 2 ? QMX_ROUTE_QMM_T_SPLITK : QMX_ROUTE_QMM_T;
     *splits = s;
     return QMX_OK;

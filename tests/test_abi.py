@@ -215,10 +215,15 @@ def test_plan_table(M, N, K, dtype, route, splits):
     assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)
 
 
-def test_plan_narrow_tiles_take_4bit_codes_only():
-    """The 32-column tiles read 4-bit codes; other widths keep the 128-column
-    tiles and their split-K partitions (capped at K / 256)."""
-    for bits in (1, 2, 3, 5, 6, 8):
+def test_plan_narrow_tiles_take_2_4_8_bit_codes():
+    """The 32-column tiles read 2-, 4- and 8-bit codes; the other widths keep the
+    128-column tiles and their split-K partitions (capped at K / 256)."""
+    for bits in (2, 8):
+        assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t", 1)
+        assert qmx.plan(16, 4096, 4096, bits, 128, BF16, num_cus=256) == ("qmm_t", 1)
+    for bits in (2, 4, 8):   # gs 32: two group epilogues per wave and block; the split plan stays
+        assert qmx.plan(16, 4096, 4096, bits, 32, BF16, num_cus=256) == ("qmm_t_splitk", 8)
+    for bits in (1, 3, 5, 6):
         assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 8)
         assert qmx.plan(16, 4096, 1024, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 4)
     # K not a multiple of 512 keeps them too

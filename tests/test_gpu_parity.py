@@ -146,27 +146,29 @@ def test_small_m_matrix_route(orc, M, N, K):
     check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=1250 + M, cols=sample_cols(N, 256, M), reruns=1)
 
 
-# (M, N, K): 4-bit unsplit qmm_t with M <= 32 and few 128-column tiles runs on
+# (M, N, K): 2/4/8-bit unsplit qmm_t with M <= 32 and few 128-column tiles runs on
 # 32-column tiles whose 8 waves split each 512-column K block: 16- and 32-row
 # tiles, ragged N, one to five blocks, K ranges whose scales and biases are
 # staged whole or per block (K / group size not a multiple of 8).
 NARROW_SHAPES = [(16, 1000, 1536), (32, 96, 2560), (9, 33, 512), (25, 4100, 1024), (1, 70, 1024)]
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dt", [qi.F16, qi.BF16])
-def test_qmm_t_narrow_tiles(orc, gs, dt):
+def test_qmm_t_narrow_tiles(orc, bits, gs, dt):
     for i, (M, N, K) in enumerate(NARROW_SHAPES):
-        check_affine(orc, "qmm_t", M, N, K, 4, gs, dt, seed=1280 + 10 * i + gs + dt, reruns=1)
+        check_affine(orc, "qmm_t", M, N, K, bits, gs, dt, seed=1280 + 10 * i + bits + gs + dt, reruns=1)
 
 
 def test_qmm_narrow_policy_shapes(orc):
     """The shapes the policy sends unsplit to 32-column tiles (they would split K
     on 128-column tiles): the config-3 M = 22 and M = 16 calls, and M = 8 of the
-    4096 x 4096 sweep, every output against the oracle."""
-    for M, N, K in ((22, 2048, 2048), (16, 4096, 4096), (8, 4096, 4096)):
-        assert qmx.plan(M, N, K, 4, 64, qi.BF16, num_cus=256) == ("qmm_t", 1)
-        check_affine(orc, "qmm", M, N, K, 4, 64, qi.BF16, seed=1290 + M, reruns=1)
+    4096 x 4096 sweep at 2, 4 and 8 bits, every output against the oracle."""
+    for M, N, K, bits in ((22, 2048, 2048, 4), (16, 4096, 4096, 4), (8, 4096, 4096, 4), (8, 4096, 4096, 8),
+                          (8, 4096, 4096, 2)):
+        assert qmx.plan(M, N, K, bits, 64, qi.BF16, num_cus=256) == ("qmm_t", 1)
+        check_affine(orc, "qmm", M, N, K, bits, 64, qi.BF16, seed=1290 + M + bits, reruns=1)
 
 
 @pytest.mark.parametrize("bits", ALL_BITS)
