@@ -40,8 +40,14 @@ int qmm_mtiles_for(int M, long long col_tiles, int cus, int K) {
 bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int cus) {
     if ((bits != 2 && bits != 4 && bits != 8) || K % 512 != 0 || M < 1 || M > 32 || splits != 1 || cus <= 0)
         return false;
-    // the 128-column tiles leave compute units idle
-    return (long long)((N + QMM_BN - 1) / QMM_BN) * batch < cus;
+    // The 128-column tiles leave compute units idle, and the narrow tiles, four
+    // times as many, take at most 3 rounds of the chip: a narrow block holds the
+    // columns of 4 wide blocks at the same cost per wave.  Measured unsplit at
+    // M = 4..7, K = 5120: N = 14336 (448 narrow tiles, 2 rounds) 18.3 us against
+    // 24.7 us on 112 wide tiles; N = 27648 (864, 4 rounds) 34.5 against 25.6 us.
+    const long long wide = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
+    const long long narrow = (long long)((N + 31) / 32) * batch;
+    return wide < cus && narrow <= 3LL * cus;
 }
 
 // A narrow work-group walks all of K (K / 512 blocks) where each partition of

@@ -34,8 +34,9 @@ int qmm_mtiles_for(int M, long long col_tiles, int cus, int K);
 int qmm_mt_for(int M, int mtiles);
 // Whether an unsplit qmm_t runs on 32-column tiles whose 8 waves split K among
 // them (one work-group per tile, 16 or 32 rows of x) instead of 128-column
-// tiles: 2-, 4- or 8-bit codes, K a multiple of 512, M <= 32, and 128-column
-// tiles that would leave some of the `cus` compute units idle.
+// tiles: 2-, 4- or 8-bit codes, K a multiple of 512, M <= 32, 128-column
+// tiles that would leave some of the `cus` compute units idle, and at most
+// 3 * cus narrow tiles.
 bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int cus);
 // Whether the dispatch policy runs such a problem unsplit on 32-column tiles
 // rather than split-K on 128-column tiles: the narrow tiles launch between a
