@@ -550,6 +550,142 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
     }
 }
 
+// ---------------------------------------------------------------- deep M = 1 form
+// M = 1, 4-bit codes, short rows (K <= QMV_DEEP_MAX_K).  A work-group of
+// QMV_DEEP_WAVES waves owns QMV_DEEP_WAVES row groups of QMV_ROWS rows, one per
+// wave, and stages the row of x in LDS once.  Every wave issues the weight,
+// scale and bias loads of all NR of its rounds (64 chunks of 32 codes each)
+// before it consumes the first, so all its rounds are in flight at once: NR is
+// a template parameter and the rounds are straight-line code, with no loop join
+// at which the compiler would wait for every outstanding load.  A lane whose
+// chunk lies past the row takes scale and bias from outside the buffer (they
+// read 0) and x = 0, so it adds exactly 0.
+constexpr int QMV_DEEP_WAVES = 4;
+constexpr int QMV_DEEP_MAX_K = 4096;   // two rounds of 64 chunks
+
+template <int DT, int GS, int NR>
+__global__ __launch_bounds__(64 * QMV_DEEP_WAVES) void qmv_deep_kernel(
+    const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
+    const void* __restrict__ x, void* __restrict__ out, int N, int K) {
+    constexpr int R = QMV_ROWS, BITS = 4;
+    using S = QmvStage<DT, BITS, GS, 1>;
+    static_assert(S::CW == 4 && S::PARTS == 1 && S::CPC == 32, "4-bit chunks of 32 codes, one group part");
+    constexpr int EB = DT == DT_F32 ? 4 : 2;               // bytes of an x, scale or bias value
+    constexpr int THREADS = 64 * QMV_DEEP_WAVES;
+    constexpr int XPIECES = QMV_DEEP_MAX_K * EB / 16;      // 16-byte pieces of the longest row of x
+    constexpr int XPT = XPIECES / THREADS;                 // x pieces per thread
+    static_assert(XPIECES % THREADS == 0 && NR * 64 * S::CPC <= QMV_DEEP_MAX_K, "x in LDS");
+    static_assert(NR * 3 * R + XPT < 64, "memory counter range");
+    constexpr int OUTSIDE = 0x7ff00000;   // past the scale and bias ranges below (a load there reads 0)
+    __shared__ __attribute__((aligned(16))) u32x4 xl[XPIECES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = blockIdx.x * QMV_DEEP_WAVES * R;      // first row of the work-group
+    const int n0 = nw + wave * R;                         // first row of this wave
+    const int G = K / GS, chunks = K / S::CPC;
+    const size_t row_bytes = (size_t)K / 2;
+
+    // 1. the row of x as 16-byte pieces (piece v at LDS slot v) into registers
+    //    first; pieces past the row repeat its last one.  They go to LDS once the
+    //    weights below are requested, so only the x loads are waited for there.
+    const int xp = K * EB / 16;
+    const __amdgpu_buffer_rsrc_t rx = buffer_over(x, (size_t)K * EB);
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j)
+        xv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, 16 * min(j * THREADS + tid, xp - 1), 0, 0));
+
+    // 2. every round's weights, scales and biases; rows past N repeat row N - 1.
+    //    The resources cover the work-group's own rows only, so OUTSIDE is past them.
+    const size_t rows = (size_t)min(N - nw, QMV_DEEP_WAVES * R);
+    const __amdgpu_buffer_rsrc_t rw =
+        buffer_over(reinterpret_cast<const unsigned char*>(w) + (size_t)nw * row_bytes, rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_over(static_cast<const unsigned char*>(scales) + (size_t)nw * G * EB, rows * G * EB);
+    const __amdgpu_buffer_rsrc_t rb =
+        buffer_over(static_cast<const unsigned char*>(biases) + (size_t)nw * G * EB, rows * G * EB);
+    uint32_t wr[NR][R][4], sr[NR][R], br[NR][R];
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int cr = lane + 64 * rd;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = min(n0 + r, N - 1) - nw;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)((size_t)rr * row_bytes) + 16 * min(cr, chunks - 1), 0, 0);
+            wr[rd][r][0] = v[0]; wr[rd][r][1] = v[1]; wr[rd][r][2] = v[2]; wr[rd][r][3] = v[3];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = min(n0 + r, N - 1) - nw;
+            const int at = cr < chunks ? (rr * G + (cr * S::CPC) / GS) * EB : OUTSIDE;
+            sr[rd][r] = buffer_raw<DT>(rs, at, 0);
+            br[rd][r] = buffer_raw<DT>(rb, at, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xl[j * THREADS + tid] = xv[j];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // 3. the rounds, in order
+    float acc[R][1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        S a;
+        const int cr = lane + 64 * rd;
+        const int xc = min(cr, chunks - 1);
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < S::XQ; ++i) a.x[0][i] = cr < chunks ? xl[S::XQ * xc + i] : zero;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.w[r][j] = wr[rd][r][j];
+            a.s[r][0] = sr[rd][r];
+            a.b[r][0] = br[rd][r];
+        }
+        qmv_consume(a, acc);
+    }
+
+    // 4. sums over the wave (fixed xor butterflies)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][0] += __shfl_xor(acc[r][0], off, 64);
+    float mine = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (lane == r) mine = acc[r][0];
+    if (lane < R && n0 + lane < N) store_elem<DT>(out, (size_t)n0 + lane, mine);
+}
+
+// Rounds per wave of the deep form (0: not used).  Measured on the chip against
+// the looped kernel (4-bit gs 64 bf16, N in 1024..14336, K in 1024..6144): the
+// deep form wins (5-14%) while the grid holds at most one work-group per CU and
+// a wave takes one round, or two rounds with at least one work-group per two
+// CUs; elsewhere the looped kernel's occupancy serves better.
+int qmv_deep_rounds(int M, int N, int K, int bits, int batch, bool plain, const void* x, int cus) {
+#ifdef QMX_NO_DEEP_QMV
+    return 0;
+#endif
+    if (M != 1 || bits != 4 || batch != 1 || !plain || K <= 0 || K > QMV_DEEP_MAX_K || N <= 0 || cus <= 0 ||
+        (reinterpret_cast<uintptr_t>(x) & 15) != 0)
+        return 0;
+    const long long wgs = ((long long)N + QMV_DEEP_WAVES * QMV_ROWS - 1) / (QMV_DEEP_WAVES * QMV_ROWS);
+    const int nr = (K / 32 + 63) / 64;
+    if (wgs > cus || (nr == 2 && 2 * wgs < cus)) return 0;
+    return nr;
+}
+
+template <int DT, int GS, int NR>
+static void qmv_deep_go(int N, int K, const uint32_t* w, const void* s, const void* b, const void* x, void* out,
+                        hipStream_t st) {
+    const dim3 grid((N + QMV_DEEP_WAVES * QMV_ROWS - 1) / (QMV_DEEP_WAVES * QMV_ROWS));
+    hipLaunchKernelGGL((qmv_deep_kernel<DT, GS, NR>), grid, dim3(64 * QMV_DEEP_WAVES), 0, st, w, s, b, x, out, N, K);
+}
+
 int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
 
 // Work split of an M = 1 matvec: KS waves of one work-group split the chunks of
@@ -618,6 +754,12 @@ static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const 
         return hipGetLastError();
     }
     const int mt = qmv_mt_for(M);
+    if constexpr (BITS == 4) {
+        const int nr = qmv_deep_rounds(M, N, K, BITS, batch, !sd.w_index && !sd.x_index, x, device_cu_count());
+        if (nr == 1) qmv_deep_go<DT, GS, 1>(N, K, w, s, b, x, out, st);
+        if (nr == 2) qmv_deep_go<DT, GS, 2>(N, K, w, s, b, x, out, st);
+        if (nr > 0) return hipGetLastError();
+    }
     if (mt == 1) {
         const QmvSplit sp = qmv_split_for(M, (long long)N * batch, K, BITS);
         switch (sp.ks * 8 + sp.rg) {

@@ -112,6 +112,21 @@ def test_qmv_work_splits(orc, N, K, bits, dt):
     check_affine(orc, "qmv", 1, N + (3 if N > 4000 else 0), K, bits, 64, dt, seed=1160 + N + K + bits)
 
 
+@pytest.mark.parametrize("N,K", [(67, 2048), (4093, 992), (1000, 1056), (2045, 4096), (4096, 2080), (3001, 4064),
+                                 (4097, 4096), (2048, 4128), (2029, 4096)])
+@pytest.mark.parametrize("gs", [32, 64, 128])
+@pytest.mark.parametrize("dt", [qi.F32, qi.F16, qi.BF16])
+def test_qmv_deep_rounds(orc, N, K, gs, dt):
+    """M = 1 rows of 4-bit codes short enough for one or two rounds of 64 chunks
+    per wave with all rounds in flight (on a 256-CU part: up to 256 work-groups
+    of 16 rows, two rounds from 128 work-groups): ragged last rounds and ragged
+    N, and the neighbours just past each limit (one work-group too many or too
+    few, K one chunk too long), which take the looped kernel."""
+    if K % gs:
+        pytest.skip("K is not a multiple of the group size")
+    check_affine(orc, "qmv", 1, N, K, 4, gs, dt, seed=1300 + N + K + gs + dt)
+
+
 @pytest.mark.parametrize("bits", ODD_BITS)
 @pytest.mark.parametrize("N,K", [(67, 256), (16384, 256), (67, 1536), (2048, 2560), (6000, 5120), (21, 14336)])
 def test_qmv_odd_width_work_splits(orc, bits, N, K):
