@@ -108,6 +108,8 @@ struct QmmCfg {
     static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
     static constexpr int RED_FLOATS = WN * MT * QMM_NB * 4 * 64;   // one K group's tiles
     static constexpr int RED_BYTES = (WK - 1) * RED_FLOATS * 4;
+    // every K group's tiles fit the stages at once: the end sum is shared by all waves
+    static constexpr bool RED_ALL = WK * RED_FLOATS * 4 <= NS * STAGE;
     static_assert(WK == 2 || (WK == 8 && (BITS == 2 || BITS == 4 || BITS == 8)), "narrow tiles: 2, 4, 8 bits");
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
@@ -570,9 +572,45 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     }
     stage_barrier<0>();
 
-    // add the other K groups' tiles to the first group's, in ascending group
-    // order, then store
+    // add the K groups' tiles in ascending group order, then store
     float* red = reinterpret_cast<float*>(smem);
+    if constexpr (C::RED_ALL) {
+        // every wave leaves its tiles in LDS; wave v then sums the values e = v,
+        // v + 8, ... of one group's tiles (value e of lane l at red[e * 64 + l],
+        // e = ((wn * MT + mf) * NB + nf) * 4 + v4) over the groups and stores them
+        constexpr int E = C::WN * MT * NB * 4;
+        static_assert(E % 8 == 0, "whole values per wave");
+#pragma unroll
+        for (int mf = 0; mf < MT; ++mf)
+#pragma unroll
+            for (int nf = 0; nf < NB; ++nf)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[wk * C::RED_FLOATS + (((wn * MT + mf) * NB + nf) * 4 + v) * 64 + lane] = run[mf][nf][v];
+        stage_barrier<0>();
+        float sum[E / 8];
+#pragma unroll
+        for (int t = 0; t < E / 8; ++t) {
+            const int e = 8 * t + wave;
+            sum[t] = red[e * 64 + lane];
+#pragma unroll
+            for (int g = 1; g < WK; ++g) sum[t] += red[g * C::RED_FLOATS + e * 64 + lane];
+        }
+#pragma unroll
+        for (int t = 0; t < E / 8; ++t) {
+            const int e = 8 * t + wave;
+            const int v = e & 3, nf = (e >> 2) % NB, mf = (e / (4 * NB)) % MT, wv = e / (4 * NB * MT);
+            const int m = m0 + mf * 16 + 4 * lgrp + v;
+            const int n = n0 + wv * (NB * 16) + nf * 16 + lrow;
+            if (m < M && n < N) {
+                if constexpr (SPLIT)
+                    ws[(((size_t)split * gridDim.y + bz) * M + m) * N + n] = sum[t];
+                else
+                    store_elem<DT>(out, (size_t)m * N + n, sum[t]);
+            }
+        }
+        return;
+    }
     if (wk > 0) {
 #pragma unroll
         for (int mf = 0; mf < MT; ++mf)

@@ -23,11 +23,13 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Round a float to bfloat16, to nearest even (NaN stays a quiet NaN).
+// Round a float to bfloat16, to nearest even (NaN stays a quiet NaN).  Both
+// results are formed and one is selected, so the conversion takes no branch.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? quiet : rounded;
 }
 
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
