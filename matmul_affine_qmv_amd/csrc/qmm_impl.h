@@ -300,14 +300,16 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const int h = blockIdx.x;
     const int L = (h & 7) * per_xcd + (h >> 3);
     if (L >= total_tiles) return;
-    const int ntile = L % ntiles;
-    const int rest = L / ntiles;
-    const int mtile = rest % mtiles;
-    const int split = rest / mtiles;
+    // unsigned 32-bit divisions throughout: every value is non-negative, and
+    // split * nkb < 2^31 (split < 16 and nkb <= K / 128)
+    const int ntile = (int)((unsigned)L % (unsigned)ntiles);
+    const int rest = (int)((unsigned)L / (unsigned)ntiles);
+    const int mtile = (int)((unsigned)rest % (unsigned)mtiles);
+    const int split = (int)((unsigned)rest / (unsigned)mtiles);
     const int n0 = ntile * C::BN, m0 = mtile * C::BM;
     const int nkb = K / C::KB;
-    const int kb0 = (int)((long)split * nkb / splits);
-    const int kb1 = (int)((long)(split + 1) * nkb / splits);
+    const int kb0 = (int)((unsigned)(split * nkb) / (unsigned)splits);
+    const int kb1 = (int)((unsigned)((split + 1) * nkb) / (unsigned)splits);
     const int nk = kb1 - kb0;
     const int G = K / GS;
     const size_t row_words = (size_t)K * BITS / 32;
@@ -543,9 +545,9 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int j = 0; j * QMM_THREADS < lanes; ++j) {
             const int v = QMM_THREADS * j + tid;
             if (v < lanes) {
-                const int which = v / (C::BN * sb_nch);
+                const int which = (int)((unsigned)v / (unsigned)(C::BN * sb_nch));
                 const int rem = v - which * (C::BN * sb_nch);
-                const int col = rem / sb_nch, ch = rem - col * sb_nch;
+                const int col = (int)((unsigned)rem / (unsigned)sb_nch), ch = rem - col * sb_nch;
                 const uint16_t* src = static_cast<const uint16_t*>(which ? biases : scales) +
                                       (size_t)min(n0 + col, N - 1) * G + 8 * (sb_c0 + min(ch, sb_last));
                 dma<16>(src, base + (QMM_THREADS * j + 64 * wave) * 16);
