@@ -181,6 +181,50 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
     mn = __builtin_amdgcn_ubfe(c, f.mn_lo, 4) | (__builtin_amdgcn_ubfe(s1, f.mn_up, 2) << 4);
 }
 
+// One round of a wave's Q4_K rows: the lanes' super-block parts against the
+// round's x (buf: its 512 pieces, swizzled by x_slot); act is false for a lane
+// whose super-block lies past the row.
+__device__ __forceinline__ void q4k_round(const u32x4* buf, bool act, const u32x4 (&hdr)[Q4K_ROWS],
+                                          const u32x4 (&qw)[Q4K_ROWS], int slot, int g, int t0,
+                                          const Q4kFields& f_lo, const Q4kFields& f_hi, float (&acc)[Q4K_ROWS]) {
+    float xlo[16], xhi[16];
+    const int u0 = (256 * slot + 64 * g + t0) / 4;   // first piece of the low half
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x_piece(buf, u0 + i, xlo + 4 * i);
+        x_piece(buf, u0 + 8 + i, xhi + 4 * i);
+    }
+    float xsl = 0.f, xsh = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { xsl += xlo[i]; xsh += xhi[i]; }
+#pragma unroll
+    for (int r = 0; r < Q4K_ROWS; ++r) {
+        const float d = f16_bits_to_f32(hdr[r].x & 0xffffu);
+        const float dmin = f16_bits_to_f32(hdr[r].x >> 16);
+        uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
+        q4k_scale_min(hdr[r].y, hdr[r].z, hdr[r].w, f_lo, sc_lo, mn_lo);
+        q4k_scale_min(hdr[r].y, hdr[r].z, hdr[r].w, f_hi, sc_hi, mn_hi);
+        float sl = 0.f, sh = 0.f;
+        const uint32_t qws[4] = {qw[r].x, qw[r].y, qw[r].z, qw[r].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
+            // keep the masked words whole so each code converts with one
+            // byte-select v_cvt_f32_ubyte<i> instead of a field extract plus a convert
+            asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sl = fmaf((float)((lo >> (8 * i)) & 0xffu), xlo[4 * k + i], sl);
+                sh = fmaf((float)((hi >> (8 * i)) & 0xffu), xhi[4 * k + i], sh);
+            }
+        }
+        const float qpart = fmaf((float)sc_lo, sl, (float)sc_hi * sh);
+        const float mpart = fmaf((float)mn_lo, xsl, (float)mn_hi * xsh);
+        const float add = fmaf(d, qpart, -dmin * mpart);
+        acc[r] += act ? add : 0.f;
+    }
+}
+
 __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __restrict__ wb,
                                                            const float* __restrict__ x,
                                                            float* __restrict__ out, int N, int K) {
@@ -205,45 +249,64 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_kernel(const uint32_t* __res
             }
         };
         blk_rounds<WS>(x, K, (nb + 7) / 8, tid, xl, load, [&](const u32x4* buf, int rd, const WS& st) {
-            const bool act = 8 * rd + slot < nb;
-            float xlo[16], xhi[16];
-            const int u0 = (256 * slot + 64 * g + t0) / 4;   // first piece of the low half
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x_piece(buf, u0 + i, xlo + 4 * i);
-                x_piece(buf, u0 + 8 + i, xhi + 4 * i);
-            }
-            float xsl = 0.f, xsh = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { xsl += xlo[i]; xsh += xhi[i]; }
-#pragma unroll
-            for (int r = 0; r < Q4K_ROWS; ++r) {
-                const float d = f16_bits_to_f32(st.hdr[r].x & 0xffffu);
-                const float dmin = f16_bits_to_f32(st.hdr[r].x >> 16);
-                uint32_t sc_lo, mn_lo, sc_hi, mn_hi;
-                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, f_lo, sc_lo, mn_lo);
-                q4k_scale_min(st.hdr[r].y, st.hdr[r].z, st.hdr[r].w, f_hi, sc_hi, mn_hi);
-                float sl = 0.f, sh = 0.f;
-                const uint32_t qws[4] = {st.qw[r].x, st.qw[r].y, st.qw[r].z, st.qw[r].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    uint32_t lo = qws[k] & 0x0f0f0f0fu, hi = (qws[k] >> 4) & 0x0f0f0f0fu;
-                    // keep the masked words whole so each code converts with one
-                    // byte-select v_cvt_f32_ubyte<i> instead of a field extract plus a convert
-                    asm volatile("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sl = fmaf((float)((lo >> (8 * i)) & 0xffu), xlo[4 * k + i], sl);
-                        sh = fmaf((float)((hi >> (8 * i)) & 0xffu), xhi[4 * k + i], sh);
-                    }
-                }
-                const float qpart = fmaf((float)sc_lo, sl, (float)sc_hi * sh);
-                const float mpart = fmaf((float)mn_lo, xsl, (float)mn_hi * xsh);
-                const float add = fmaf(d, qpart, -dmin * mpart);
-                acc[r] += act ? add : 0.f;
-            }
+            q4k_round(buf, 8 * rd + slot < nb, st.hdr, st.qw, slot, g, t0, f_lo, f_hi, acc);
         });
     }
+    blk_store(acc, lane, n0, N, out);
+}
+
+// Short rows (at most NR rounds of 8 super-blocks): the whole row of x is staged
+// in LDS once, and every wave issues the header and quant loads of all its
+// rounds before consuming the first, as straight-line code (NR is a template
+// parameter), so no round waits on another's loads.
+constexpr int Q4K_DEEP_MAX_ROUNDS = 4;
+
+template <int NR>
+__global__ __launch_bounds__(BLK_THREADS) void q4_k_deep_kernel(const uint32_t* __restrict__ wb,
+                                                                const float* __restrict__ x,
+                                                                float* __restrict__ out, int N, int K) {
+    constexpr int XPIECES = NR * BLK_ROUND / 4;           // 16-byte x pieces of the longest row
+    constexpr int XPT = XPIECES / BLK_THREADS;
+    static_assert(XPT * BLK_THREADS == XPIECES && XPT + 2 * NR * Q4K_ROWS < 64, "x pieces; memory counter range");
+    __shared__ u32x4 xl[XPIECES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = lane >> 3, part = lane & 7;
+    const int g = part >> 1, t0 = (part & 1) * 16;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * Q4K_ROWS;
+    const int nb = K / 256, xp = K / 4;
+    const Q4kFields f_lo = q4k_fields(2 * g), f_hi = q4k_fields(2 * g + 1);
+
+    // 1. x pieces into registers (pieces past the row repeat its last one)
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j)
+        xv[j] = *reinterpret_cast<const u32x4*>(x + 4 * min(j * BLK_THREADS + tid, xp - 1));
+    // keep the x loads ahead of the weight loads (loads complete in order, so the
+    // wait before the LDS store then leaves every weight load in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. every round's headers and quants (blocks past the row repeat its last one)
+    u32x4 hdr[NR][Q4K_ROWS], qw[NR][Q4K_ROWS];
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int b = min(8 * rd + slot, nb - 1);
+#pragma unroll
+        for (int r = 0; r < Q4K_ROWS; ++r) {
+            const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 36;
+            hdr[rd][r] = *reinterpret_cast<const u32x4*>(blk);
+            qw[rd][r] = *reinterpret_cast<const u32x4*>(blk + 4 + 4 * part);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. x to LDS (the compiler waits for the x loads only), one barrier
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xl[x_slot(j * BLK_THREADS + tid)] = xv[j];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // 4. the rounds in order (round rd's x starts at piece 512 rd; the swizzle
+    //    repeats every 256 pieces, so x_slot addresses it relative to that start)
+    float acc[Q4K_ROWS] = {};
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd)
+        q4k_round(xl + rd * (BLK_ROUND / 4), 8 * rd + slot < nb, hdr[rd], qw[rd], slot, g, t0, f_lo, f_hi, acc);
     blk_store(acc, lane, n0, N, out);
 }
 
@@ -255,7 +318,25 @@ hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int
 
 hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
     const dim3 grid((N + BLK_WAVES * Q4K_ROWS - 1) / (BLK_WAVES * Q4K_ROWS));
-    hipLaunchKernelGGL(q4_k_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
+    // Measured against the looped kernel (N = 4096..27648, K = 2048..8192): the
+    // deep form is 1-13% faster, except at three rounds (176 registers, 2 waves
+    // per SIMD) on grids beyond three work-groups per CU (27648 x 5120: 5% slower).
+    const int rounds = (K / 256 + 7) / 8;
+    const bool deep = K >= 256 && rounds <= Q4K_DEEP_MAX_ROUNDS && (rounds != 3 || (long long)grid.x <= 3LL * device_cu_count());
+#ifdef QMX_NO_DEEP_Q4K
+    if (false) {
+#else
+    if (deep) {
+#endif
+        switch (rounds) {
+            case 1: hipLaunchKernelGGL(q4_k_deep_kernel<1>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+            case 2: hipLaunchKernelGGL(q4_k_deep_kernel<2>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+            case 3: hipLaunchKernelGGL(q4_k_deep_kernel<3>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+            default: hipLaunchKernelGGL(q4_k_deep_kernel<4>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+        }
+    } else {
+        hipLaunchKernelGGL(q4_k_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
+    }
     return hipGetLastError();
 }
 

@@ -383,7 +383,8 @@ def test_q4_k_config5(orc):
     assert_close(y.cpu().numpy().astype(np.float64), orc.q4_k(c["blocks"], c["x"], N, K), qi.F32, orc, "q4_k")
 
 
-@pytest.mark.parametrize("NK", [(1, 256), (7, 512), (21, 768), (33, 1280), (45, 2560), (130, 4096)])
+@pytest.mark.parametrize("NK", [(1, 256), (7, 512), (21, 768), (33, 1280), (45, 2560), (130, 4096), (67, 6144),
+                                (9, 7936), (40, 8192), (5, 8448), (3, 12800)])
 def test_blocks_small_ragged(orc, NK):
     N, K = NK
     say("blocks", N, K)
