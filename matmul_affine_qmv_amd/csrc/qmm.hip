@@ -52,20 +52,29 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
 
 // A narrow work-group walks all of K (K / 512 blocks) where each partition of
 // the split 128-column plan walks K / (128 S) blocks of the same cost per wave;
-// the narrow call saves the accumulate kernel and its launch instead.  Measured
-// per call at M = 8..32, N = 1024..14336, K = 2048..8192 on 256 CUs: narrow is
-// up to 1.4x faster while it walks at most 4 blocks more than a partition,
-// even at 6, and 8-25% slower from 8 on at 32 rows.  At gs 32 each wave
-// carries two group epilogues per block, and narrow tiles were 1-6% slower than
-// the split plan at M = 8, N = K = 4096 (2, 4 and 8 bits), so they are not
-// preferred there.
+// the narrow call saves the accumulate kernel and its launch instead.  Both
+// plans run one work-group per CU at a time, so each walks its blocks once per
+// round of the chip.  Measured per call at M = 8..32, N = 1024..14336, K =
+// 2048..8192 on 256 CUs: narrow is up to 1.4x faster while it walks at most 4
+// blocks more than the split plan, even at 6, and 8-25% slower from 8 on at 32
+// rows.  Two rounds of narrow tiles pay the work-group's fixed costs twice; they
+// measured 1-5% faster than the split plan at K = 4096 and 5120 (N = 11008,
+// 14336, 16384: 8-10 blocks per round) but 3-17% slower at K = 8192 and 12288
+// (16384 x 8192: 29.1 against 24.9 us), so they are taken only while a
+// work-group walks at most 10 blocks.  At gs 32
+// each wave carries two group epilogues per block, and narrow tiles were 1-6%
+// slower than the split plan at M = 8, N = K = 4096 (2, 4 and 8 bits), so they
+// are not preferred there.
 bool qmm_narrow_preferred(int M, int N, int K, int bits, int gs, long long batch, int cus) {
     if (gs < 64 || !qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
     const long long tiles = (long long)((N + 31) / 32) * batch;
-    if (4 * tiles < cus || tiles > cus) return false;
+    if (4 * tiles < cus || tiles > 2LL * cus || (tiles > cus && K / 512 > 10)) return false;
     const long long wide = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
-    const int s = qmm_policy_splits(wide * qmm_mtiles_for(M, wide, cus, K), K, cus);
-    return K / 512 - K / (QMM_KB * s) <= 6;
+    const long long wide_tiles = wide * qmm_mtiles_for(M, wide, cus, K);
+    const int s = qmm_policy_splits(wide_tiles, K, cus);
+    const long long narrow_blocks = (tiles + cus - 1) / cus * (K / 512);
+    const long long split_blocks = (wide_tiles * s + cus - 1) / cus * (K / (QMM_KB * s));
+    return narrow_blocks - split_blocks <= 6;
 }
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,

@@ -99,14 +99,18 @@ int device_cus() {
 // the chip (N x K from 2048 x 2048 to 14336 x 5120, M = 2..7, 4-bit gs 64):
 // about 2.5 us plus 0.16, 0.28 or 0.45 us per million codes for M = 2, 3..4
 // and 5..7.  Where 32-column tiles apply, the matrix route has one work-group
-// walk all of K: about 4.5 us plus 0.95 us per 1024 columns of K; otherwise
-// it costs about its weight bytes at 2.3 TB/s with a floor of about 9 us.
+// walk all of K: about 3.5 us plus 1.1 us per 1024 columns of K for each round
+// of the chip the tiles take (4096 x 4096: 7.9 us, 14336 x 4096 in two rounds:
+// 15.0-15.6 us); otherwise it costs about its weight bytes at 2.3 TB/s with a
+// floor of about 9 us.
 bool small_m_prefers_matrix(int M, int N, int K, int bits, int gs, int batch, int cus) {
     if (M < 2 || M >= 8) return false;
-    const double mcodes = (double)N * K * (batch > 0 ? batch : 1) / 1e6;
+    const int b = batch > 0 ? batch : 1;
+    const double mcodes = (double)N * K * b / 1e6;
     const double t_qmv = 2.5 + (M == 2 ? 0.16 : M <= 4 ? 0.28 : 0.45) * mcodes;
-    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, gs, batch > 0 ? batch : 1, cus)
-                             ? 4.5 + 0.95 * K / 1024.0
+    const long long rounds = ((long long)(N + 31) / 32 * b + cus - 1) / cus;
+    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, gs, b, cus)
+                             ? (double)rounds * (3.5 + 1.1 * K / 1024.0)
                              : std::max(9.0, mcodes * 1e6 * bits / 8.0 / 2.3e6);
     return t_mat < t_qmv;
 }

@@ -201,10 +201,11 @@ def test_block_validation():
     (384, 4096, 4096, BF16, "qmm_t", 1),             # 64-row tiles: 6 x 32 = 192 groups, as many as 3 x 32 split 2
     (257, 16384, 4096, F16, "qmm_t", 1),             # 3 x 128 tiles >= 256 CUs
     (8, 4096, 4096, F16, "qmm_t", 1),
-    (16, 14336, 4096, BF16, "qmm_t_splitk", 2),      # 448 narrow tiles would not all be resident
+    (16, 14336, 4096, BF16, "qmm_t", 1),             # two rounds of 448 narrow tiles, 8 blocks each
+    (16, 16384, 8192, BF16, "qmm_t_splitk", 2),      # ... but not at 16 blocks per round
     (16, 4096, 4032, BF16, "qmv", 1),                # K % 128 != 0 -> qmv
     (2, 14336, 5120, BF16, "qmv", 1),                # M = 2..7: qmv while its vector work is small
-    (4, 14336, 5120, BF16, "qmm_t_splitk", 2),       # ... the matrix route once it is not
+    (4, 14336, 5120, BF16, "qmm_t", 1),              # ... the matrix route once it is not
     (7, 27648, 5120, BF16, "qmm_t", 1),
     (5, 5120, 5120, F16, "qmm_t", 1),
     (4, 5120, 5120, BF16, "qmm_t", 1),               # measured: 32-column tiles 9.5 us, qmv 12.1 us

@@ -178,10 +178,11 @@ def test_qmm_t_narrow_tiles(orc, bits, gs, dt):
 
 def test_qmm_narrow_policy_shapes(orc):
     """The shapes the policy sends unsplit to 32-column tiles (they would split K
-    on 128-column tiles): the config-3 M = 22 and M = 16 calls, and M = 8 of the
-    4096 x 4096 sweep at 2, 4 and 8 bits, every output against the oracle."""
+    on 128-column tiles): the config-3 M = 22 and M = 16 calls, M = 8 of the
+    4096 x 4096 sweep at 2, 4 and 8 bits, and 14336 x 4096, whose 448 tiles take
+    two rounds of the chip, every output against the oracle."""
     for M, N, K, bits in ((22, 2048, 2048, 4), (16, 4096, 4096, 4), (8, 4096, 4096, 4), (8, 4096, 4096, 8),
-                          (8, 4096, 4096, 2)):
+                          (8, 4096, 4096, 2), (16, 14336, 4096, 4)):
         assert qmx.plan(M, N, K, bits, 64, qi.BF16, num_cus=256) == ("qmm_t", 1)
         check_affine(orc, "qmm", M, N, K, bits, 64, qi.BF16, seed=1290 + M + bits, reruns=1)
 
