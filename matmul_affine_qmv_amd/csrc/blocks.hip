@@ -3,15 +3,15 @@
 // Formats and arithmetic follow page "hanzo-kernel src/quant.rs" (Q8_0
 // packed layout: 9 words per 32 weights; Q4_K: 144-byte super-blocks with
 // 6-bit sub-block scales and mins).  Both kernels are weight-bandwidth
-// bound.  A work-group of 4 waves owns 8 output rows per wave for Q8_0 and
-// 5 for Q4_K (both at 3 waves per SIMD, so N = 14336 runs in one generation
-// of resident work-groups; more rows per wave keep more of a wave's loads in
-// flight per round trip), and walks
-// K in rounds of 2048 values: the round's float32 x is loaded once per
-// work-group (two 16-byte loads per thread) and shared through LDS, so x
-// costs a quarter of a weight row's worth of loads instead of as much as the
-// weights themselves.  Accumulation is float32 and each row ends with a
-// fixed-order wave reduction.
+// bound.  Rows of up to 6144 (Q8_0) or 8192 (Q4_K) values take a deep form: a
+// work-group of 4 waves stages the whole row of float32 x in LDS once, and
+// every wave issues the loads of all its rounds before consuming the first,
+// as straight-line code (2 rows per wave for Q8_0, 5 for Q4_K).  Longer rows
+// take the looped form: 8 rows per wave for Q8_0 and 5 for Q4_K (both at 3
+// waves per SIMD), walking K in rounds of 2048 values whose x is loaded once
+// per work-group (two 16-byte loads per thread) and shared through LDS, with
+// the next round's weights requested while the current one is consumed.
+// Accumulation is float32 and each row ends with a fixed-order wave reduction.
 #include "qmx_device.h"
 #include "qmx_internal.h"
 
@@ -102,6 +102,33 @@ __device__ __forceinline__ void blk_store(float (&acc)[ROWS], int lane, int n0, 
 // of the round).  A signed byte q is read as the unsigned byte q ^ 0x80 =
 // q + 128, and the 128 * sum(x) it adds is taken off once per block:
 // sum_i q_i x_i = sum_i (q_i + 128) x_i - 128 sum_i x_i.
+// One round of a wave's Q8_0 rows: lane l's block of each row against the
+// round's x (buf: its 512 pieces, swizzled by x_slot); act is false for a lane
+// whose block lies past the row.
+template <int ROWS>
+__device__ __forceinline__ void q8_0_round(const u32x4* buf, bool act, const uint32_t (&w)[ROWS][9], int lane,
+                                           float (&acc)[ROWS]) {
+    float xv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x_piece(buf, 8 * lane + i, xv + 4 * i);
+    float xs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xs += xv[i];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const float d = f16_bits_to_f32(w[r][0] & 0xffffu);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t wd = w[r][1 + j] ^ 0x80808080u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s = fmaf((float)((wd >> (8 * i)) & 0xffu), xv[4 * j + i], s);
+        }
+        const float add = d * fmaf(-128.f, xs, s);
+        acc[r] += act ? add : 0.f;
+    }
+}
+
 __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __restrict__ wb,
                                                            const float* __restrict__ x,
                                                            float* __restrict__ out, int N, int K) {
@@ -123,28 +150,57 @@ __global__ __launch_bounds__(BLK_THREADS) void q8_0_kernel(const uint32_t* __res
             }
         };
         blk_rounds<WS>(x, K, (nb + 63) / 64, tid, xl, load, [&](const u32x4* buf, int rd, const WS& st) {
-            const bool act = 64 * rd + lane < nb;
-            float xv[32];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x_piece(buf, 8 * lane + i, xv + 4 * i);
-            float xs = 0.f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i) xs += xv[i];
-#pragma unroll
-            for (int r = 0; r < Q8_ROWS; ++r) {
-                const float d = f16_bits_to_f32(st.w[r][0] & 0xffffu);
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t wd = st.w[r][1 + j] ^ 0x80808080u;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s = fmaf((float)((wd >> (8 * i)) & 0xffu), xv[4 * j + i], s);
-                }
-                const float add = d * fmaf(-128.f, xs, s);
-                acc[r] += act ? add : 0.f;
-            }
+            q8_0_round<Q8_ROWS>(buf, 64 * rd + lane < nb, st.w, lane, acc);
         });
     }
+    blk_store(acc, lane, n0, N, out);
+}
+
+// Short rows (at most NR rounds of 64 blocks) with Q8_DEEP_ROWS rows per wave:
+// the whole row of x is staged in LDS once and every wave issues the loads of
+// all its rounds before consuming the first (as the deep Q4_K form below).
+// Measured against the looped kernel over N = 4096..27648, K = 2048..6144: 1.1-
+// 1.6x faster at 2 rows per wave (14336 x 5120: 20.2 -> 17.9 us); 1, 3, 4 and
+// 6 rows were up to 9% slower than 2.
+constexpr int Q8_DEEP_ROWS = 2;
+constexpr int Q8_DEEP_MAX_ROUNDS = 3;
+
+template <int NR>
+__global__ __launch_bounds__(BLK_THREADS) void q8_0_deep_kernel(const uint32_t* __restrict__ wb,
+                                                                const float* __restrict__ x,
+                                                                float* __restrict__ out, int N, int K) {
+    constexpr int R = Q8_DEEP_ROWS;
+    constexpr int XPIECES = NR * BLK_ROUND / 4;
+    constexpr int XPT = XPIECES / BLK_THREADS;
+    static_assert(XPT * BLK_THREADS == XPIECES && XPT + 9 * NR * R < 64 * 4, "x pieces");
+    __shared__ u32x4 xl[XPIECES];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = (blockIdx.x * BLK_WAVES + wave) * R;
+    const int nb = K / 32, xp = K / 4;
+
+    u32x4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j)
+        xv[j] = *reinterpret_cast<const u32x4*>(x + 4 * min(j * BLK_THREADS + tid, xp - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t w[NR][R][9];
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) {
+        const int b = min(64 * rd + lane, nb - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t* blk = wb + ((size_t)min(n0 + r, N - 1) * nb + b) * 9;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) w[rd][r][j] = blk[j];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xl[x_slot(j * BLK_THREADS + tid)] = xv[j];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float acc[R] = {};
+#pragma unroll
+    for (int rd = 0; rd < NR; ++rd) q8_0_round<R>(xl + rd * (BLK_ROUND / 4), 64 * rd + lane < nb, w[rd], lane, acc);
     blk_store(acc, lane, n0, N, out);
 }
 
@@ -311,6 +367,18 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_deep_kernel(const uint32_t* 
 }
 
 hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
+    const int rounds = (K / 32 + 63) / 64;
+#ifndef QMX_NO_DEEP_Q8
+    if (K >= 32 && rounds <= Q8_DEEP_MAX_ROUNDS) {
+        const dim3 grid((N + BLK_WAVES * Q8_DEEP_ROWS - 1) / (BLK_WAVES * Q8_DEEP_ROWS));
+        switch (rounds) {
+            case 1: hipLaunchKernelGGL(q8_0_deep_kernel<1>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+            case 2: hipLaunchKernelGGL(q8_0_deep_kernel<2>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+            default: hipLaunchKernelGGL(q8_0_deep_kernel<3>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
+        }
+        return hipGetLastError();
+    }
+#endif
     const dim3 grid((N + BLK_WAVES * Q8_ROWS - 1) / (BLK_WAVES * Q8_ROWS));
     hipLaunchKernelGGL(q8_0_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
