@@ -144,12 +144,12 @@ __device__ __forceinline__ void unpack_word(uint32_t w, float (&q)[32 / BITS]) {
     }
 }
 
-// Registers of one chunk: the R rows' weight chunks (CW words each), their
+// Registers of one chunk: the RR rows' weight chunks (CW words each), their
 // scales and biases (raw storage bits), and the MT rows' x values under the
 // chunk.
-template <int DT, int BITS, int GS, int MT>
+template <int DT, int BITS, int GS, int MT, int RR = QMV_ROWS>
 struct QmvStage {
-    static constexpr int R = QMV_ROWS;
+    static constexpr int R = RR;
     static constexpr int CW = qmv_chunk_words(BITS);
     static constexpr int CPC = qmv_chunk_codes(BITS);
     static constexpr int PARTS = CPC > GS ? CPC / GS : 1;
@@ -260,10 +260,9 @@ __device__ __forceinline__ uint32_t stream_pair(const uint32_t (&w)[CW], int e, 
     return p;
 }
 
-template <int DT, int BITS, int GS, int MT>
-__device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT>& st,
-                                            float (&acc)[QMV_ROWS][MT]) {
-    using S = QmvStage<DT, BITS, GS, MT>;
+template <int DT, int BITS, int GS, int MT, int RR>
+__device__ __forceinline__ void qmv_consume(const QmvStage<DT, BITS, GS, MT, RR>& st, float (&acc)[RR][MT]) {
+    using S = QmvStage<DT, BITS, GS, MT, RR>;
     constexpr int R = S::R;
     constexpr int PARTS = S::PARTS;
     constexpr int WPP = 4 / PARTS;          // words per group part
@@ -551,30 +550,29 @@ __global__ __launch_bounds__(64 * KSPLIT) void qmv_kernel(const uint32_t* __rest
 }
 
 // ---------------------------------------------------------------- deep M = 1 form
-// M = 1, 4-bit codes, short rows (K <= QMV_DEEP_MAX_K).  A work-group of
-// QMV_DEEP_WAVES waves owns QMV_DEEP_WAVES row groups of QMV_ROWS rows, one per
-// wave, and stages the row of x in LDS once.  Every wave issues the weight,
-// scale and bias loads of all NR of its rounds (64 chunks of 32 codes each)
-// before it consumes the first, so all its rounds are in flight at once: NR is
-// a template parameter and the rounds are straight-line code, with no loop join
-// at which the compiler would wait for every outstanding load.  A lane whose
-// chunk lies past the row takes scale and bias from outside the buffer (they
-// read 0) and x = 0, so it adds exactly 0.
+// M = 1, 4-bit codes, short rows (at most NR rounds of 64 chunks of 32 codes).
+// A work-group of QMV_DEEP_WAVES waves owns QMV_DEEP_WAVES row groups of RW
+// rows, one per wave, and stages the row of x in LDS once.  Every wave issues
+// the weight, scale and bias loads of all NR of its rounds before it consumes
+// the first, so all its rounds are in flight at once: NR is a template
+// parameter and the rounds are straight-line code, with no loop join at which
+// the compiler would wait for every outstanding load.  A lane whose chunk lies
+// past the row takes scale and bias from outside the buffer (they read 0) and
+// x = 0, so it adds exactly 0.
 constexpr int QMV_DEEP_WAVES = 4;
-constexpr int QMV_DEEP_MAX_K = 4096;   // two rounds of 64 chunks
 
-template <int DT, int GS, int NR>
+template <int DT, int GS, int NR, int RW>
 __global__ __launch_bounds__(64 * QMV_DEEP_WAVES) void qmv_deep_kernel(
     const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
     const void* __restrict__ x, void* __restrict__ out, int N, int K) {
-    constexpr int R = QMV_ROWS, BITS = 4;
-    using S = QmvStage<DT, BITS, GS, 1>;
+    constexpr int R = RW, BITS = 4;
+    using S = QmvStage<DT, BITS, GS, 1, RW>;
     static_assert(S::CW == 4 && S::PARTS == 1 && S::CPC == 32, "4-bit chunks of 32 codes, one group part");
     constexpr int EB = DT == DT_F32 ? 4 : 2;               // bytes of an x, scale or bias value
     constexpr int THREADS = 64 * QMV_DEEP_WAVES;
-    constexpr int XPIECES = QMV_DEEP_MAX_K * EB / 16;      // 16-byte pieces of the longest row of x
+    constexpr int XPIECES = NR * 64 * S::CPC * EB / 16;   // 16-byte pieces of the longest row of x
     constexpr int XPT = XPIECES / THREADS;                 // x pieces per thread
-    static_assert(XPIECES % THREADS == 0 && NR * 64 * S::CPC <= QMV_DEEP_MAX_K, "x in LDS");
+    static_assert(XPIECES % THREADS == 0, "x copies per thread");
     static_assert(NR * 3 * R + XPT < 64, "memory counter range");
     constexpr int OUTSIDE = 0x7ff00000;   // past the scale and bias ranges below (a load there reads 0)
     __shared__ __attribute__((aligned(16))) u32x4 xl[XPIECES];
@@ -661,29 +659,57 @@ __global__ __launch_bounds__(64 * QMV_DEEP_WAVES) void qmv_deep_kernel(
     if (lane < R && n0 + lane < N) store_elem<DT>(out, (size_t)n0 + lane, mine);
 }
 
-// Rounds per wave of the deep form (0: not used).  Measured on the chip against
-// the looped kernel (4-bit gs 64 bf16, N in 1024..14336, K in 1024..6144): the
-// deep form wins (5-14%) while the grid holds at most one work-group per CU and
-// a wave takes one round, or two rounds with at least one work-group per two
-// CUs; elsewhere the looped kernel's occupancy serves better.
-int qmv_deep_rounds(int M, int N, int K, int bits, int batch, bool plain, const void* x, int cus) {
-#ifdef QMX_NO_DEEP_QMV
-    return 0;
-#endif
-    if (M != 1 || bits != 4 || batch != 1 || !plain || K <= 0 || K > QMV_DEEP_MAX_K || N <= 0 || cus <= 0 ||
+// The deep form's rounds and rows per wave for an M = 1 call (rounds 0: not
+// used).  Measured on the chip against the looped kernel:
+// * 16-bit x (4-bit gs 64 bf16, N in 1024..14336, K in 1024..6144): with 4
+//   rows per wave the deep form wins (5-14%) while the grid holds at most one
+//   work-group per CU and a wave takes one round, or two rounds with at least
+//   one work-group per two CUs; elsewhere the looped kernel's occupancy serves
+//   better (also with 1 or 2 rows per wave: 3-20% slower at N = 14336, 27648).
+// * float32 x (two or three rounds): 4 rows per wave from two work-groups per
+//   CU on (11008 x 4096: 11.6 -> 9.6 us, 27648 x 5120: 29.4 -> 26.6 us), 2 rows
+//   per wave from two work-groups of 8 rows per CU (5120 x 5120: 9.0 ->
+//   8.6 us); seven rounds (K = 14336) lost with 1 and 2 rows per wave.
+struct QmvDeep {
+    int nr, rw;
+};
+QmvDeep qmv_deep_for(int M, int N, int K, int bits, int dt, int batch, bool plain, const void* x, int cus) {
+    if (M != 1 || bits != 4 || batch != 1 || !plain || K <= 0 || N <= 0 || cus <= 0 ||
         (reinterpret_cast<uintptr_t>(x) & 15) != 0)
-        return 0;
-    const long long wgs = ((long long)N + QMV_DEEP_WAVES * QMV_ROWS - 1) / (QMV_DEEP_WAVES * QMV_ROWS);
+        return {0, 0};
     const int nr = (K / 32 + 63) / 64;
-    if (wgs > cus || (nr == 2 && 2 * wgs < cus)) return 0;
-    return nr;
+    const long long n = N;
+    if (dt == DT_F32 && (nr == 2 || nr == 3)) {
+        if (n >= 2LL * cus * QMV_DEEP_WAVES * 4) return {nr, 4};
+        if (n >= 2LL * cus * QMV_DEEP_WAVES * 2) return {nr, 2};
+    }
+    const long long wgs = (n + QMV_DEEP_WAVES * 4 - 1) / (QMV_DEEP_WAVES * 4);
+    if (nr > 2 || wgs > cus || (nr == 2 && 2 * wgs < cus)) return {0, 0};
+    return {nr, 4};
 }
 
-template <int DT, int GS, int NR>
+template <int DT, int GS, int NR, int RW>
 static void qmv_deep_go(int N, int K, const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                         hipStream_t st) {
-    const dim3 grid((N + QMV_DEEP_WAVES * QMV_ROWS - 1) / (QMV_DEEP_WAVES * QMV_ROWS));
-    hipLaunchKernelGGL((qmv_deep_kernel<DT, GS, NR>), grid, dim3(64 * QMV_DEEP_WAVES), 0, st, w, s, b, x, out, N, K);
+    const dim3 grid((N + QMV_DEEP_WAVES * RW - 1) / (QMV_DEEP_WAVES * RW));
+    hipLaunchKernelGGL((qmv_deep_kernel<DT, GS, NR, RW>), grid, dim3(64 * QMV_DEEP_WAVES), 0, st, w, s, b, x, out, N,
+                       K);
+}
+
+template <int DT, int GS>
+static bool qmv_deep_launch(QmvDeep d, int N, int K, const uint32_t* w, const void* s, const void* b, const void* x,
+                            void* out, hipStream_t st) {
+    if (d.nr == 1 && d.rw == 4) qmv_deep_go<DT, GS, 1, 4>(N, K, w, s, b, x, out, st);
+    else if (d.nr == 2 && d.rw == 4) qmv_deep_go<DT, GS, 2, 4>(N, K, w, s, b, x, out, st);
+    else if constexpr (DT == DT_F32) {
+        if (d.nr == 3 && d.rw == 4) qmv_deep_go<DT, GS, 3, 4>(N, K, w, s, b, x, out, st);
+        else if (d.nr == 2 && d.rw == 2) qmv_deep_go<DT, GS, 2, 2>(N, K, w, s, b, x, out, st);
+        else if (d.nr == 3 && d.rw == 2) qmv_deep_go<DT, GS, 3, 2>(N, K, w, s, b, x, out, st);
+        else return false;
+    } else {
+        return false;
+    }
+    return true;
 }
 
 int qmv_mt_for(int M) { return M >= 3 ? 4 : (M == 2 ? 2 : 1); }
@@ -755,10 +781,8 @@ static hipError_t qmv_mt(const uint32_t* w, const void* s, const void* b, const 
     }
     const int mt = qmv_mt_for(M);
     if constexpr (BITS == 4) {
-        const int nr = qmv_deep_rounds(M, N, K, BITS, batch, !sd.w_index && !sd.x_index, x, device_cu_count());
-        if (nr == 1) qmv_deep_go<DT, GS, 1>(N, K, w, s, b, x, out, st);
-        if (nr == 2) qmv_deep_go<DT, GS, 2>(N, K, w, s, b, x, out, st);
-        if (nr > 0) return hipGetLastError();
+        const QmvDeep d = qmv_deep_for(M, N, K, BITS, DT, batch, !sd.w_index && !sd.x_index, x, device_cu_count());
+        if (d.nr > 0 && qmv_deep_launch<DT, GS>(d, N, K, w, s, b, x, out, st)) return hipGetLastError();
     }
     if (mt == 1) {
         const QmvSplit sp = qmv_split_for(M, (long long)N * batch, K, BITS);

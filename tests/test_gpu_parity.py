@@ -113,13 +113,14 @@ def test_qmv_work_splits(orc, N, K, bits, dt):
 
 
 @pytest.mark.parametrize("N,K", [(67, 2048), (4093, 992), (1000, 1056), (2045, 4096), (4096, 2080), (3001, 4064),
-                                 (4097, 4096), (2048, 4128), (2029, 4096)])
+                                 (4097, 4096), (2048, 4128), (2029, 4096), (8195, 4160), (4100, 6144), (8192, 6176)])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dt", [qi.F32, qi.F16, qi.BF16])
 def test_qmv_deep_rounds(orc, N, K, gs, dt):
-    """M = 1 rows of 4-bit codes short enough for one or two rounds of 64 chunks
-    per wave with all rounds in flight (on a 256-CU part: up to 256 work-groups
-    of 16 rows, two rounds from 128 work-groups): ragged last rounds and ragged
+    """M = 1 rows of 4-bit codes short enough for all rounds of 64 chunks per wave
+    in flight (on a 256-CU part, 16-bit x: up to 256 work-groups of 16 rows,
+    two rounds from 128 work-groups; float32 x: two or three rounds with 4 rows
+    per wave from N = 8192, 2 rows from N = 4096): ragged last rounds and ragged
     N, and the neighbours just past each limit (one work-group too many or too
     few, K one chunk too long), which take the looped kernel."""
     if K % gs:
