@@ -365,8 +365,11 @@ def kernels_of(c, route, splits):
         # one launch sequence for the whole batch, timed as a whole
         return [(f"qmm_{c['route']} (whole call)", lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), c["M"] >= 8)]
     if c["kind"] != "affine" or route != "qmm_t_splitk":
-        label = {"qmv": "qmv_kernel", "qmm_t": "qmm_t_kernel", "q8_0": "q8_0_kernel",
-                 "q4_k": "q4_k_kernel", "q8_i8": "q8_i8_kernel"}[route if c["kind"] == "affine" else c["kind"]]
+        # the M = 1 matvecs and the block matvecs have a looped and a deep form,
+        # chosen by shape inside the library: the label names both
+        label = {"qmv": "qmv_kernel|qmv_deep_kernel", "qmm_t": "qmm_t_kernel",
+                 "q8_0": "q8_0_kernel|q8_0_deep_kernel", "q4_k": "q4_k_kernel|q4_k_deep_kernel",
+                 "q8_i8": "q8_i8_kernel"}[route if c["kind"] == "affine" else c["kind"]]
         return [(label, lambda d, c=c: launch(c, d), alg_bytes(c), flops(c), route == "qmm_t")]
     kw = dict(bits=c["bits"], group_size=c["gs"], splits=splits)
     return [
