@@ -368,7 +368,6 @@ __global__ __launch_bounds__(BLK_THREADS) void q4_k_deep_kernel(const uint32_t* 
 
 hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int K, hipStream_t st) {
     const int rounds = (K / 32 + 63) / 64;
-#ifndef QMX_NO_DEEP_Q8
     if (K >= 32 && rounds <= Q8_DEEP_MAX_ROUNDS) {
         const dim3 grid((N + BLK_WAVES * Q8_DEEP_ROWS - 1) / (BLK_WAVES * Q8_DEEP_ROWS));
         switch (rounds) {
@@ -378,7 +377,6 @@ hipError_t launch_q8_0(const uint32_t* w, const float* x, float* out, int N, int
         }
         return hipGetLastError();
     }
-#endif
     const dim3 grid((N + BLK_WAVES * Q8_ROWS - 1) / (BLK_WAVES * Q8_ROWS));
     hipLaunchKernelGGL(q8_0_kernel, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K);
     return hipGetLastError();
@@ -391,11 +389,7 @@ hipError_t launch_q4_k(const uint32_t* w, const float* x, float* out, int N, int
     // per SIMD) on grids beyond three work-groups per CU (27648 x 5120: 5% slower).
     const int rounds = (K / 256 + 7) / 8;
     const bool deep = K >= 256 && rounds <= Q4K_DEEP_MAX_ROUNDS && (rounds != 3 || (long long)grid.x <= 3LL * device_cu_count());
-#ifdef QMX_NO_DEEP_Q4K
-    if (false) {
-#else
     if (deep) {
-#endif
         switch (rounds) {
             case 1: hipLaunchKernelGGL(q4_k_deep_kernel<1>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
             case 2: hipLaunchKernelGGL(q4_k_deep_kernel<2>, grid, dim3(BLK_THREADS), 0, st, w, x, out, N, K); break;
