@@ -67,14 +67,20 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
 // are not preferred there.
 bool qmm_narrow_preferred(int M, int N, int K, int bits, int gs, long long batch, int cus) {
     if (gs < 64 || !qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
-    const long long tiles = (long long)((N + 31) / 32) * batch;
+    // 16-column tiles where they fit one round, else 32-column tiles
+    const long long t16 = (long long)((N + 15) / 16) * batch;
+    const bool cols16 = t16 <= cus;
+    const long long tiles = cols16 ? t16 : (long long)((N + 31) / 32) * batch;
     if (4 * tiles < cus || tiles > 2LL * cus || (tiles > cus && K / 512 > 10)) return false;
     const long long wide = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
     const long long wide_tiles = wide * qmm_mtiles_for(M, wide, cus, K);
     const int s = qmm_policy_splits(wide_tiles, K, cus);
-    const long long narrow_blocks = (tiles + cus - 1) / cus * (K / 512);
+    // a block of a 16-column tile (half the matrix work) weighs 0.7 of a block of
+    // the 128-column split plan (measured over N = 1024..4096, K = 2048..8192,
+    // M = 4..32: within 3% of the best route where the blocks are close)
+    const double narrow_blocks = (double)((tiles + cus - 1) / cus) * (K / 512) * (cols16 ? 0.7 : 1.0);
     const long long split_blocks = (wide_tiles * s + cus - 1) / cus * (K / (QMM_KB * s));
-    return narrow_blocks - split_blocks <= 6;
+    return narrow_blocks <= (double)split_blocks + 6.0;
 }
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,

@@ -53,13 +53,15 @@ namespace qmx {
 // WK: groups of waves along K.  Each of the 8 waves takes two k-steps (64
 // columns) of every K block, so a block is KB = 64 * WK columns, and the
 // 8 / WK waves of one group own NB fragments of 16 columns each: WK = 2 is the
-// 128-column tile, WK = 8 a 32-column tile for narrow problems (more
-// work-groups from few columns, every K group summed in the work-group).
-template <int DT, int BITS, int GS, int MT, bool SBV, int WK = 2>
+// 128-column tile, WK = 8 a 32-column (NB = 2) or 16-column (NB = 1) tile for
+// narrow problems (more work-groups from few columns, every K group summed in
+// the work-group).
+template <int DT, int BITS, int GS, int MT, bool SBV, int WK = 2, int NBT = QMM_NB>
 struct QmmCfg {
     static constexpr int BM = 16 * MT;
     static constexpr int WN = 8 / WK;                         // waves along N
-    static constexpr int BN = WN * QMM_NB * 16;               // columns per tile
+    static constexpr int NB = NBT;                            // 16-column fragments per wave
+    static constexpr int BN = WN * NB * 16;                   // columns per tile
     static constexpr int KB = 64 * WK;                        // columns per K block
     static constexpr int GPB = KB / GS;                       // groups per K block
     static constexpr int KS = GS / 32;                        // MFMA k-steps per group
@@ -84,8 +86,13 @@ struct QmmCfg {
     // copy slots per W row: 4-byte words for 1- and 2-bit codes, else 16-byte pieces
     static constexpr int W_SLOTS = W4B ? W_ROW / 4 : W_ROW / 16;
     static constexpr int W_PIECES = W_BYTES / 16;
-    static constexpr int WPT = W4B ? W_BYTES / (4 * QMM_THREADS)
-                             : WREP ? (W_PIECES + QMM_THREADS - 1) / QMM_THREADS : W_BYTES / (16 * QMM_THREADS);
+    // wave-wide W copies per stage (2, 4, 8 bits); fewer than 8 (16-column tiles of
+    // 4-bit codes) are made by waves 0 .. W_WAVES - 1 only
+    static constexpr int W_WCOPIES = W_BYTES / (64 * (W4B ? 4 : 16));
+    static constexpr int W_WAVES = (WREP || BITS == 1 || W_WCOPIES >= 8) ? 8 : W_WCOPIES;
+    static constexpr int WPT = W4B && BITS == 1 ? W_BYTES / (4 * QMM_THREADS)
+                             : WREP ? (W_PIECES + QMM_THREADS - 1) / QMM_THREADS
+                             : (W_WCOPIES + 7) / 8;
     // Scales then biases.  Staged per block, one 16-bit value per lane
     // (zero-extended to 4 bytes in LDS), unless SBV: then the work-group's whole
     // K range of both is copied once, before the ring, in 16-byte chunks.
@@ -97,6 +104,7 @@ struct QmmCfg {
     static constexpr int RING_LDS = 160 * 1024 - (SBV ? 12 * 1024 : 0);
     static constexpr int NS = RING_LDS / STAGE < 4 ? RING_LDS / STAGE : 4;
     static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
+    static constexpr int LPS_NW = XPT + SBPT;                 // ... in waves that copy no W
     // SBV: 16-byte chunks (8 groups) per (scale/bias, column) held in LDS
     static constexpr int SBV_CHUNKS = SBV ? ((160 * 1024 - NS * STAGE) / (2 * BN * 16) > 15
                                                  ? 15 : (160 * 1024 - NS * STAGE) / (2 * BN * 16))
@@ -106,23 +114,24 @@ struct QmmCfg {
     // Offset the expanded bf16 codes carry: 128 + q (q < 128); 8-bit bf16 codes are
     // converted instead, and f16 codes have their 1024 removed exactly before the MFMA.
     static constexpr float OFF = (CVT8 || DT == DT_F16) ? 0.f : 128.f;
-    static constexpr int RED_FLOATS = WN * MT * QMM_NB * 4 * 64;   // one K group's tiles
+    static constexpr int RED_FLOATS = WN * MT * NB * 4 * 64;   // one K group's tiles
     static constexpr int RED_BYTES = (WK - 1) * RED_FLOATS * 4;
     // every K group's tiles fit the stages at once: the end sum is shared by all waves
-    static constexpr bool RED_ALL = WK * RED_FLOATS * 4 <= NS * STAGE;
+    static constexpr bool RED_ALL = WK * RED_FLOATS * 4 <= NS * STAGE && (WN * MT * NB * 4) % 8 == 0;
     static_assert(WK == 2 || (WK == 8 && (BITS == 2 || BITS == 4 || BITS == 8)), "narrow tiles: 2, 4, 8 bits");
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
     static_assert(STAGE % 1024 == 0 && X_BYTES % 1024 == 0, "stage alignment");
     static_assert(WREP ? W_PIECES % 64 == 0 && WPT * QMM_THREADS >= W_PIECES
-                       : WPT * QMM_THREADS * (W4B ? 4 : 16) == W_BYTES, "W copies per thread");
+                       : WPT * W_WAVES * 64 * (W4B ? 4 : 16) == W_BYTES, "W copies per thread");
+    static_assert(NB == QMM_NB || (WK == 8 && NB == 1 && !WREP && BITS != 1), "16-column tiles: narrow, 2/4/8 bits");
     static_assert(!SBV || SBV_CHUNKS >= 3, "room for the staged scales and biases");
 };
 
 // Largest chunk count the staged scale/bias copy of one work-group may need.
-template <int DT, int BITS, int GS, int MT, int WK = 2>
-constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true, WK>::SBV_CHUNKS; }
+template <int DT, int BITS, int GS, int MT, int WK = 2, int NBT = QMM_NB>
+constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true, WK, NBT>::SBV_CHUNKS; }
 
 // Bank spread of 2-, 4- and 8-bit W rows of SLOTS copy slots: slot p of row R
 // holds piece (or word) p ^ w_swz(R) of the row.  The 128-column rows (4, 8 and
@@ -278,12 +287,12 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK>
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK, int NBT>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const uint32_t* __restrict__ w, const void* __restrict__ scales, const void* __restrict__ biases,
     const void* __restrict__ x, void* __restrict__ out, float* __restrict__ ws, QmxStrides sd,
     int M, int N, int K, int splits, int ntiles, int mtiles, int total_tiles, int per_xcd) {
-    using C = QmmCfg<DT, BITS, GS, MT, SBV, WK>;
+    using C = QmmCfg<DT, BITS, GS, MT, SBV, WK, NBT>;
     // problem blockIdx.y of the batch (16-bit x, scales, biases and out)
     const long long bz = blockIdx.y, wz = qmx_w_matrix(sd, bz), xz = qmx_x_matrix(sd, bz);
     w += wz * sd.w;
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     x = static_cast<const uint16_t*>(x) + xz * sd.x;
     if constexpr (!SPLIT) out = static_cast<uint16_t*>(out) + bz * M * (long long)N;
     const long long XR = sd.x_row;
-    constexpr int NB = QMM_NB;
+    constexpr int NB = C::NB;
     constexpr int NS = C::NS;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * C::STAGE + C::SBV_BYTES];
 
@@ -389,6 +398,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int i = 0; i < C::XPT; ++i) dma<16>(xsrc[i] + (size_t)kb * C::KB, X + (8 * i + wave) * 1024);
 #pragma unroll
         for (int j = 0; j < C::WPT; ++j) {
+            if (C::W_WAVES < 8 && wave >= C::W_WAVES) continue;   // wave-uniform
             if constexpr (C::W4B)
                 dma<4>(wsrc[j] + (size_t)kb * (C::W_ROW / 4), Wl + (8 * j + wave) * 256);
             else if constexpr (C::WREP)
@@ -563,10 +573,14 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         for (int j = 0; j < NS; ++j) {
             const int i = base + j;
             if (i < nk) {
-                if (i + NS - 2 < nk)
-                    stage_barrier<C::LPS * (NS - 2)>();
-                else
+                if (i + NS - 2 < nk) {
+                    if (C::W_WAVES == 8 || wave < C::W_WAVES)
+                        stage_barrier<C::LPS * (NS - 2)>();
+                    else
+                        stage_barrier<C::LPS_NW * (NS - 2)>();
+                } else {
                     stage_barrier<0>();
+                }
                 if (i + NS - 1 < nk) stage_load(kb0 + i + NS - 1, (j + NS - 1) % NS);
                 compute(j, kb0 + i);
             }
@@ -658,19 +672,19 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
         }
 }
 
-template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK>
+template <int DT, int BITS, int GS, int MT, bool SPLIT, bool SBV, int WK, int NBT>
 void qmm_go(dim3 grid, const uint32_t* w, const void* s, const void* b, const void* x, void* out, float* ws,
             QmxStrides sd, int M, int N, int K, int splits, int ntiles, int mtiles, int total, int per_xcd,
             hipStream_t st) {
-    hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV, WK>), grid, dim3(QMM_THREADS), 0, st, w, s, b,
-                       x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd);
+    hipLaunchKernelGGL((qmm_t_kernel<DT, BITS, GS, MT, SPLIT, SBV, WK, NBT>), grid, dim3(QMM_THREADS), 0, st, w, s,
+                       b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd);
 }
 
-template <int DT, int BITS, int GS, int MT, int WK = 2>
+template <int DT, int BITS, int GS, int MT, int WK = 2, int NBT = QMM_NB>
 hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const void* x, void* out,
                          float* ws, int batch, QmxStrides sd, int M, int N, int K, int splits, int mtiles,
                          hipStream_t st) {
-    using C = QmmCfg<DT, BITS, GS, MT, false, WK>;
+    using C = QmmCfg<DT, BITS, GS, MT, false, WK, NBT>;
     const int ntiles = (N + C::BN - 1) / C::BN;
     const int total = ntiles * mtiles * splits;
     const int per_xcd = (total + 7) / 8;
@@ -683,9 +697,9 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
     const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
                          (sd.sb * 2) % 16 == 0;
     const bool sbv = aligned && K > 0 && G % 8 == 0 &&
-                     (nk_max * C::GPB + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT, WK>();
+                     (nk_max * C::GPB + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT, WK, NBT>();
 #define QMM_GO(SPLIT_, SBV_) \
-    qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_, WK>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
+    qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_, WK, NBT>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
     if constexpr (WK == 2) {
         if (splits > 1) {
             if (sbv) QMM_GO(true, true);
@@ -706,6 +720,13 @@ hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const 
     if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
         // narrow tiles: one tile of 16 or 32 rows
         if (qmm_narrow(M, N, K, BITS, batch, splits, device_cu_count())) {
+            // 16-column tiles while they fit one round of the chip: twice the
+            // work-groups, each with half the matrix work per block (measured 11-23%
+            // faster than 32-column tiles at M = 8..32, N = 1024..4096, K = 2048..8192)
+            if ((long long)((N + 15) / 16) * batch <= device_cu_count()) {
+                if (M <= 16) return qmm_launch_mt<DT, BITS, GS, 1, 8, 1>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
+                return qmm_launch_mt<DT, BITS, GS, 2, 8, 1>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
+            }
             if (M <= 16) return qmm_launch_mt<DT, BITS, GS, 1, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
             return qmm_launch_mt<DT, BITS, GS, 2, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
         }

@@ -96,22 +96,36 @@ int device_cus() {
 
 // Below M = 8 qmv reads each weight once for up to 4 rows of x, and makes a
 // second pass for M > 4; a pass costs the same for 3 and 4 rows.  Measured on
-// the chip (N x K from 2048 x 2048 to 14336 x 5120, M = 2..7, 4-bit gs 64):
-// about 2.5 us plus 0.16, 0.28 or 0.45 us per million codes for M = 2, 3..4
-// and 5..7.  Where 32-column tiles apply, the matrix route has one work-group
-// walk all of K: about 3.5 us plus 1.1 us per 1024 columns of K for each round
-// of the chip the tiles take (4096 x 4096: 7.9 us, 14336 x 4096 in two rounds:
-// 15.0-15.6 us); otherwise it costs about its weight bytes at 2.3 TB/s with a
-// floor of about 9 us.
+// the chip (N x K from 1024 x 4096 to 14336 x 5120, M = 2..7, 4-bit gs 64):
+// * where 16-column tiles apply (N / 16 tiles fit one round of the chip), the
+//   matrix route walks K at about 3.4 us plus 0.8 us per 1024 columns of K and
+//   beat qmv from M = 3 on at every measured shape (4096 x 4096, M = 4: 6.8
+//   against 8.0 us); at M = 2 qmv costs about 2.5 us plus 0.16 us per million
+//   codes, but at least 2.5 us plus 0.65 us per 1024 columns of K, and won at
+//   every measured shape (2048 x 8192: 8.0 against 9.2 us);
+// * otherwise qmv costs about 2.5 us plus 0.16, 0.28 or 0.45 us per million
+//   codes for M = 2, 3..4 and 5..7 (at least 2.5 us plus 0.65 us, from M = 3
+//   3 us plus 0.8 us, per 1024 columns of K: 2048 x 8192, M = 4: 10.3 us), and
+//   the matrix route 3.5 us plus 1.1 us per
+//   1024 columns of K for each round of the chip its 32-column tiles take
+//   (14336 x 4096 in two rounds: 15.0-15.6 us), or, without narrow tiles,
+//   about its weight bytes at 2.3 TB/s with a floor of about 9 us.
 bool small_m_prefers_matrix(int M, int N, int K, int bits, int gs, int batch, int cus) {
     if (M < 2 || M >= 8) return false;
     const int b = batch > 0 ? batch : 1;
     const double mcodes = (double)N * K * b / 1e6;
-    const double t_qmv = 2.5 + (M == 2 ? 0.16 : M <= 4 ? 0.28 : 0.45) * mcodes;
-    const long long rounds = ((long long)(N + 31) / 32 * b + cus - 1) / cus;
-    const double t_mat = qmx::qmm_narrow_preferred(M, N, K, bits, gs, b, cus)
-                             ? (double)rounds * (3.5 + 1.1 * K / 1024.0)
-                             : std::max(9.0, mcodes * 1e6 * bits / 8.0 / 2.3e6);
+    const bool narrow = qmx::qmm_narrow_preferred(M, N, K, bits, gs, b, cus);
+    if (narrow && (long long)((N + 15) / 16) * b <= cus) {
+        if (M >= 3) return true;
+        return 3.4 + 0.8 * K / 1024.0 < std::max(2.5 + 0.16 * mcodes, 2.5 + 0.65 * K / 1024.0);
+    }
+    const double t_qmv = std::max(2.5 + (M == 2 ? 0.16 : M <= 4 ? 0.28 : 0.45) * mcodes,
+                                  M == 2 ? 2.5 + 0.65 * K / 1024.0 : 3.0 + 0.8 * K / 1024.0);
+    double t_mat = std::max(9.0, mcodes * 1e6 * bits / 8.0 / 2.3e6);
+    if (narrow) {
+        const long long rounds = ((long long)(N + 31) / 32 * b + cus - 1) / cus;
+        t_mat = (double)rounds * (3.5 + 1.1 * K / 1024.0);
+    }
     return t_mat < t_qmv;
 }
 
