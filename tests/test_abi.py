@@ -211,6 +211,12 @@ def test_block_validation():
     (4, 5120, 5120, BF16, "qmm_t", 1),               # measured: 32-column tiles 9.5 us, qmv 12.1 us
     (7, 2048, 2048, BF16, "qmm_t", 1),              # 16-column tiles: 5.0 us against 6.1 us for qmv
     (7, 14336, 5120, F32, "qmv", 1),                 # float32 stays on qmv at every M
+    (16, 1024, 4096, BF16, "qmm_t", 1),              # 64 16-column tiles: 6.6 us against 8.1 split in 16
+    (16, 4096, 8192, BF16, "qmm_t", 1),              # 16 blocks of 16 columns: 10.4 us against 12.6 split in 8
+    (16, 1024, 8192, BF16, "qmm_t_splitk", 16),      # ... 9.6 us against 9.2 split in 16
+    (2, 2048, 8192, BF16, "qmv", 1),                 # M = 2 stays on qmv where 16-column tiles apply
+    (5, 2048, 2048, BF16, "qmm_t", 1),               # from M = 3 they take the matrix route (5.0 against 6.0 us)
+    (4, 2048, 8192, BF16, "qmm_t_splitk", 16),       # qmv walks a long K slowly (10.3 us against 9.5)
 ])
 def test_plan_table(M, N, K, dtype, route, splits):
     assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)
