@@ -119,10 +119,11 @@ int qmx_qmm_t(const uint32_t* w_packed, const void* scales, const void* biases,
 
 /* qmx_qmm_t_splitk -- qmx_qmm_t with K split into `splits` partitions
  * (page "mlx PR 4682": split-K kernel writing float32 partials that a
- * separate accumulate kernel sums, rounding once).  Partition p covers the
- * 128-column K blocks [floor(p*nkb/splits), floor((p+1)*nkb/splits)) with
- * nkb = K/128; each partition must hold at least two blocks (256 columns),
- * so 2 <= splits <= min(QMX_MAX_SPLITS, K/256).  The first kernel writes
+ * separate accumulate kernel sums, rounding once).  K is cut into segments
+ * of 256 columns (of 128 columns when K is not a multiple of 256), and
+ * partition p covers segments [floor(p*nseg/splits), floor((p+1)*nseg/splits))
+ * with nseg = K/segment; each partition must hold at least 256 columns, so
+ * 2 <= splits <= min(QMX_MAX_SPLITS, K/256).  The first kernel writes
  * workspace[p][m][n] (float32); the second sums p = 0..splits-1 in that
  * order and rounds once to `dtype`.  workspace: device memory of at least
  * qmx_splitk_workspace_bytes(M, N, splits) bytes, 16-byte aligned, owned by

@@ -50,6 +50,21 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
     return wide < cus && narrow <= 3LL * cus;
 }
 
+// Split-K on 64-column tiles (the 8 waves as 4 K groups of 2 column waves over
+// 256-column K blocks): per block the same work as a 128-column tile, so with
+// half the partitions a work-group walks as many blocks, and the partials and
+// their accumulate halve.  Measured against 128-column tiles at twice the
+// partitions: (17408, 5120, 56) 30.8 against 32.0 us, (10752, 2048, 85) 17.5
+// against 18.5, (4096, 4096, 64) 13.4 against 16.9, (4096, 4096, 128) 17.7
+// against 20.3, (5120, 5120, 48) 14.3 against 16.1; taken while the tiles of
+// all partitions fit one round of the chip (at twice that they lost 10-20%).
+bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus) {
+    if ((bits != 2 && bits != 4 && bits != 8) || K % 256 != 0 || M < 1 || M > 192 || splits < 2 || cus <= 0)
+        return false;
+    const long long tiles = (long long)((N + 63) / 64) * ((M + 63) / 64) * batch;
+    return tiles * splits <= cus;
+}
+
 // A narrow work-group walks all of K (K / 512 blocks) where each partition of
 // the split 128-column plan walks K / (128 S) blocks of the same cost per wave;
 // the narrow call saves the accumulate kernel and its launch instead.  Both

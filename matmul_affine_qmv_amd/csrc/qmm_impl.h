@@ -13,6 +13,11 @@
 //   each).  Waves 0-3 each own 2 fragments of 16 columns and take k-steps
 //   0-1 of every block; waves 4-7 own the same columns and take k-steps 2-3.
 //   The two halves add their float32 tiles through LDS once at the end.
+//   Narrower tiles regroup the same 8 waves along K (WK groups): 64-column
+//   tiles over 256-column blocks (WK = 4, split-K partials) and 32- or
+//   16-column tiles over 512-column blocks (WK = 8, unsplit).
+// * A split-K partition covers whole segments of K: 256 columns when K is a
+//   multiple of 256, else 128, the same segments on every tile width.
 // * Every operand of a K block (x rows, packed W rows, raw 16-bit scales and
 //   biases) is copied from HBM straight into an LDS stage by the global-to-LDS
 //   form of the load (no register staging, no conversion on the way in),
@@ -53,9 +58,10 @@ namespace qmx {
 // WK: groups of waves along K.  Each of the 8 waves takes two k-steps (64
 // columns) of every K block, so a block is KB = 64 * WK columns, and the
 // 8 / WK waves of one group own NB fragments of 16 columns each: WK = 2 is the
-// 128-column tile, WK = 8 a 32-column (NB = 2) or 16-column (NB = 1) tile for
-// narrow problems (more work-groups from few columns, every K group summed in
-// the work-group).
+// 128-column tile, WK = 4 a 64-column tile of 256-column K blocks (split-K with
+// half the partitions of the 128-column plan), WK = 8 a 32-column (NB = 2) or
+// 16-column (NB = 1) tile for narrow problems (more work-groups from few
+// columns, every K group summed in the work-group).
 template <int DT, int BITS, int GS, int MT, bool SBV, int WK = 2, int NBT = QMM_NB>
 struct QmmCfg {
     static constexpr int BM = 16 * MT;
@@ -118,7 +124,7 @@ struct QmmCfg {
     static constexpr int RED_BYTES = (WK - 1) * RED_FLOATS * 4;
     // every K group's tiles fit the stages at once: the end sum is shared by all waves
     static constexpr bool RED_ALL = WK * RED_FLOATS * 4 <= NS * STAGE && (WN * MT * NB * 4) % 8 == 0;
-    static_assert(WK == 2 || (WK == 8 && (BITS == 2 || BITS == 4 || BITS == 8)), "narrow tiles: 2, 4, 8 bits");
+    static_assert(WK == 2 || ((WK == 4 || WK == 8) && (BITS == 2 || BITS == 4 || BITS == 8)), "64- and 32/16-column tiles: 2, 4, 8 bits");
     static_assert(NS >= 3, "at least two stages in flight");
     static_assert(RED_BYTES <= NS * STAGE, "end reduction reuses the stages");
     static_assert(LPS * (NS - 2) < 64, "memory counter range");
@@ -316,9 +322,12 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_t_kernel(
     const int mtile = (int)((unsigned)rest % (unsigned)mtiles);
     const int split = (int)((unsigned)rest / (unsigned)mtiles);
     const int n0 = ntile * C::BN, m0 = mtile * C::BM;
-    const int nkb = K / C::KB;
-    const int kb0 = (int)((unsigned)(split * nkb) / (unsigned)splits);
-    const int kb1 = (int)((unsigned)((split + 1) * nkb) / (unsigned)splits);
+    // K partitions in segments of 256 columns (128 when K is not a multiple of
+    // 256), whatever the block size: partition p covers segments
+    // [floor(p * nseg / splits), floor((p + 1) * nseg / splits))
+    const int seg = (K & 255) == 0 ? 256 : 128, nseg = K / seg;
+    const int kb0 = (int)((unsigned)(split * nseg) / (unsigned)splits) * seg / C::KB;
+    const int kb1 = (int)((unsigned)((split + 1) * nseg) / (unsigned)splits) * seg / C::KB;
     const int nk = kb1 - kb0;
     const int G = K / GS;
     const size_t row_words = (size_t)K * BITS / 32;
@@ -700,7 +709,7 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
                      (nk_max * C::GPB + 7) / 8 + 2 <= qmm_sbv_chunks<DT, BITS, GS, MT, WK, NBT>();
 #define QMM_GO(SPLIT_, SBV_) \
     qmm_go<DT, BITS, GS, MT, SPLIT_, SBV_, WK, NBT>(grid, w, s, b, x, out, ws, sd, M, N, K, splits, ntiles, mtiles, total, per_xcd, st)
-    if constexpr (WK == 2) {
+    if constexpr (WK != 8) {
         if (splits > 1) {
             if (sbv) QMM_GO(true, true);
             else QMM_GO(true, false);
@@ -729,6 +738,21 @@ hipError_t qmm_launch_gs(const uint32_t* w, const void* s, const void* b, const 
             }
             if (M <= 16) return qmm_launch_mt<DT, BITS, GS, 1, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
             return qmm_launch_mt<DT, BITS, GS, 2, 8>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, 1, st);
+        }
+    }
+    if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
+        // split-K on 64-column tiles of 256-column blocks while those fit one
+        // round of the chip
+        if (splits > 1 && qmm_wide64(M, N, K, BITS, batch, splits, device_cu_count())) {
+            const int t64 = (M + 63) / 64;
+#define QMM_64(MT_) qmm_launch_mt<DT, BITS, GS, MT_, 4>(w, s, b, x, out, ws, batch, sd, M, N, K, splits, t64, st)
+            switch (qmm_mt_for(M, t64)) {
+                case 1: return QMM_64(1);
+                case 2: return QMM_64(2);
+                case 3: return QMM_64(3);
+                default: return QMM_64(4);
+            }
+#undef QMM_64
         }
     }
     const int mt = qmm_mtiles_for(M, (long long)((N + QMM_BN - 1) / QMM_BN) * batch, device_cu_count(), K);

@@ -38,6 +38,8 @@ int qmm_mt_for(int M, int mtiles);
 // tiles that would leave some of the `cus` compute units idle, and at most
 // 3 * cus narrow tiles.
 bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int cus);
+// Split-K partitions run on 64-column tiles of 256-column blocks.
+bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus);
 // Whether the dispatch policy runs such a problem unsplit on 32-column tiles
 // rather than split-K on 128-column tiles: the narrow tiles launch between a
 // quarter of the compute units and all of them, K is short enough for one

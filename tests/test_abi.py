@@ -188,12 +188,12 @@ def test_block_validation():
     (16, 4096, 768, BF16, "qmm_t", 1),
     (16, 4096, 1024, BF16, "qmm_t", 1),              # 2 narrow blocks against 2 blocks + the accumulate
     (22, 2048, 2048, BF16, "qmm_t", 1),              # 64 32-column tiles, 4 blocks each
-    (22, 2048, 8192, BF16, "qmm_t_splitk", 16),      # 16 narrow blocks: too long for one work-group
-    (40, 2048, 2048, BF16, "qmm_t_splitk", 8),       # M > 32 stays on 128-column tiles
-    (85, 2048, 10752, BF16, "qmm_t_splitk", 8),       # 2 M tiles of 43 rows x 16 N tiles
-    (128, 4096, 4096, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 N tiles
-    (33, 4096, 14336, BF16, "qmm_t_splitk", 8),
-    (56, 5120, 17408, BF16, "qmm_t_splitk", 6),      # floor(256 / 40 tiles)
+    (22, 2048, 8192, BF16, "qmm_t_splitk", 8),       # 16 narrow blocks: too long; 32 64-column tiles x 8
+    (40, 2048, 2048, BF16, "qmm_t_splitk", 8),       # M > 32: 32 64-column tiles x 8 partitions
+    (85, 2048, 10752, BF16, "qmm_t_splitk", 4),      # 2 M tiles of 64 rows x 32 64-column tiles
+    (128, 4096, 4096, BF16, "qmm_t_splitk", 2),      # 2 M tiles of 64 rows x 64 64-column tiles
+    (33, 4096, 14336, BF16, "qmm_t_splitk", 4),
+    (56, 5120, 17408, BF16, "qmm_t_splitk", 3),      # floor(256 / 80 64-column tiles)
     (512, 4096, 4096, BF16, "qmm_t", 1),             # 64-row tiles: 8 M tiles x 32 N tiles fill 256 CUs
     (1024, 4096, 4096, BF16, "qmm_t", 1),            # 128-row tiles: 8 x 32
     (512, 1024, 4096, BF16, "qmm_t_splitk", 4),      # 64-row tiles, 8 x 8 = 64 tiles: 4 partitions
@@ -216,7 +216,7 @@ def test_block_validation():
     (16, 1024, 8192, BF16, "qmm_t_splitk", 16),      # ... 9.6 us against 9.2 split in 16
     (2, 2048, 8192, BF16, "qmv", 1),                 # M = 2 stays on qmv where 16-column tiles apply
     (5, 2048, 2048, BF16, "qmm_t", 1),               # from M = 3 they take the matrix route (5.0 against 6.0 us)
-    (4, 2048, 8192, BF16, "qmm_t_splitk", 16),       # qmv walks a long K slowly (10.3 us against 9.5)
+    (4, 2048, 8192, BF16, "qmm_t_splitk", 8),        # qmv walks a long K slowly
 ])
 def test_plan_table(M, N, K, dtype, route, splits):
     assert qmx.plan(M, N, K, 4, 64, dtype, num_cus=256) == (route, splits)
@@ -228,8 +228,9 @@ def test_plan_narrow_tiles_take_2_4_8_bit_codes():
     for bits in (2, 8):
         assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t", 1)
         assert qmx.plan(16, 4096, 4096, bits, 128, BF16, num_cus=256) == ("qmm_t", 1)
-    for bits in (2, 4, 8):   # gs 32: two group epilogues per wave and block; the split plan stays
-        assert qmx.plan(16, 4096, 4096, bits, 32, BF16, num_cus=256) == ("qmm_t_splitk", 8)
+    for bits in (2, 4, 8):   # gs 32: two group epilogues per wave and block; the split plan stays,
+        # on 64 64-column tiles x 4 partitions
+        assert qmx.plan(16, 4096, 4096, bits, 32, BF16, num_cus=256) == ("qmm_t_splitk", 4)
     for bits in (1, 3, 5, 6):
         assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 8)
         assert qmx.plan(16, 4096, 1024, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 4)
@@ -247,9 +248,10 @@ def test_plan_respects_split_limits():
         qmx.plan(16, 4096, 96, 2, 32, F32, 256)      # qmv route cannot take 192-bit rows
     with pytest.raises(qmx.QmxError):
         qmx.plan(1, 4096, 4096, 7, 64, BF16, 256)      # 7-bit codes are not a supported width
-    for bits in (1, 3, 5, 6):                          # the other widths route like 4-bit on 128-column tiles
-        assert qmx.plan(1, 4096, 4096, bits, 64, BF16, 256) == ("qmv", 1)
-        assert qmx.plan(40, 4096, 4096, bits, 64, BF16, 256) == qmx.plan(40, 4096, 4096, 4, 64, BF16, 256)
+    for bits in (1, 3, 5, 6):                          # the other widths take the same routes; their split
+        assert qmx.plan(1, 4096, 4096, bits, 64, BF16, 256) == ("qmv", 1)      # plans stay on 128-column tiles
+        assert qmx.plan(40, 4096, 4096, bits, 64, BF16, 256) == ("qmm_t_splitk", 8)
+    assert qmx.plan(40, 4096, 4096, 4, 64, BF16, 256) == ("qmm_t_splitk", 4)   # 64 64-column tiles x 4
 
 
 def test_binding_rejects_cpu_tensors():

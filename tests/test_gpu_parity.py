@@ -225,22 +225,33 @@ def test_qmm_config3_every_route(orc, KNM, route):
                      splits=int(route[1:]))
 
 
-def test_splitk_partials_match_partition_oracle(orc):
-    """workspace[p] is the float32 partial of partition p: its K blocks are
-    [floor(p*nkb/S), floor((p+1)*nkb/S)) of 128 columns."""
-    M, N, K, bits, gs, dt, S = 22, 256, 1792, 4, 64, qi.BF16, 3
+def partition_groups(K, S, p, gs):
+    """Groups [g0, g1) of split-K partition p: K in segments of 256 columns (128
+    when K is not a multiple of 256), partition p taking segments
+    [floor(p*nseg/S), floor((p+1)*nseg/S))."""
+    seg = 256 if K % 256 == 0 else 128
+    nseg = K // seg
+    return (p * nseg // S) * seg // gs, ((p + 1) * nseg // S) * seg // gs
+
+
+# (M, N, K, S): 64-column tiles (tiles x S within one round of a 256-CU part),
+# 128-column tiles (N = 8192: beyond it), and K not a multiple of 256
+@pytest.mark.parametrize("M,N,K,S", [(22, 256, 1792, 3), (56, 256, 4352, 5), (22, 8192, 1792, 3), (22, 256, 1152, 3),
+                                     (85, 320, 2560, 4)])
+def test_splitk_partials_match_partition_oracle(orc, M, N, K, S):
+    """workspace[p] is the float32 partial of partition p over its segments of
+    K, on either tile width."""
+    bits, gs, dt = 4, 64, qi.BF16
     say("splitk partials", M, N, K, S)
     c = qi.affine_case(M, N, K, bits, gs, dt, seed=1500)
     w, s, b, x = to_dev(c)
     ws = torch.empty(S * M * N, dtype=torch.float32, device=DEV)
     y = qmx.qmm_t_splitk(w, s, b, x, bits=bits, group_size=gs, splits=S, workspace=ws)
     torch.cuda.synchronize()
-    nkb = K // 128
     parts = ws.view(S, M, N).cpu().numpy().astype(np.float64)
     for p in range(S):
-        kb0, kb1 = p * nkb // S, (p + 1) * nkb // S
-        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs,
-                                kb0 * 128 // gs, kb1 * 128 // gs)
+        g0, g1 = partition_groups(K, S, p, gs)
+        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs, g0, g1)
         assert_close(parts[p], ref, qi.F32, orc, what=f"partial {p}")
     # the output is the rounded sum of the partials in ascending order
     acc = parts[0].astype(np.float32)
@@ -272,12 +283,10 @@ def test_partials_and_accumulate_entry_points(orc, bits, gs, dt):
     assert torch.equal(parts.reshape(-1).view(torch.int32), ws_a.view(torch.int32))
     assert torch.equal(out.view(torch.int16), y.view(torch.int16))
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
-    nkb = K // 128
     host = parts.cpu().numpy().astype(np.float64)
     for p in range(S):
-        kb0, kb1 = p * nkb // S, (p + 1) * nkb // S
-        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs,
-                                kb0 * 128 // gs, kb1 * 128 // gs)
+        g0, g1 = partition_groups(K, S, p, gs)
+        ref = orc.affine_groups(c["w"], c["scales"], c["biases"], dt, c["x"], dt, M, N, K, bits, gs, g0, g1)
         assert_close(host[p], ref, qi.F32, orc, what=f"partial {p}")
 
 
@@ -341,9 +350,12 @@ def test_splitk_ragged_partitions(orc, bits, gs):
 
 
 def test_splitk_many_m_tiles(orc):
-    """Split-K with three 128-row tiles of x (M = 300) and a ragged last tile."""
+    """Split-K with three 128-row tiles of x (M = 300) and a ragged last tile,
+    and with three 64-row tiles on 64-column tiles (M = 150, 2/4/8 bits)."""
     check_affine(orc, "splitk", 300, 384, 2048, 4, 64, qi.BF16, seed=1800, splits=4, reruns=1)
     check_affine(orc, "splitk", 300, 200, 2560, 4, 32, qi.F16, seed=1801, splits=5)
+    for bits, gs, dt in ((4, 64, qi.BF16), (8, 32, qi.F16), (2, 128, qi.BF16)):
+        check_affine(orc, "splitk", 150, 320, 3072, bits, gs, dt, seed=1802 + bits, splits=4)
 
 
 # ---------------------------------------------------------------- affine sweep (bits x gs x dtype x M)
