@@ -76,15 +76,20 @@ bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int 
 // measured 1-5% faster than the split plan at K = 4096 and 5120 (N = 11008,
 // 14336, 16384: 8-10 blocks per round) but 3-17% slower at K = 8192 and 12288
 // (16384 x 8192: 29.1 against 24.9 us), so they are taken only while a
-// work-group walks at most 10 blocks.  At gs 32
-// each wave carries two group epilogues per block, and narrow tiles were 1-6%
-// slower than the split plan at M = 8, N = K = 4096 (2, 4 and 8 bits), so they
-// are not preferred there.
+// work-group walks at most 10 blocks.  At gs 32 each wave carries two group
+// epilogues per block, which weighs more on the narrow tiles: measured at M =
+// 8..32 (4-bit, and 16 rows at 2 and 8 bits), 16-column tiles were 8-34%
+// faster than the split plan with up to 2 blocks more (4096 x 4096: 8.1 against
+// 8.9 us at M = 8; 2048 x 2048: 5.2 against 6.6), 10-16% slower with 3 or more
+// (1024 x 4096, 4096 x 8192), and 32-column tiles 15-22% slower even at equal
+// blocks (14336 x 4096), so at gs 32 only 16-column tiles within 2 blocks are
+// taken.
 bool qmm_narrow_preferred(int M, int N, int K, int bits, int gs, long long batch, int cus) {
-    if (gs < 64 || !qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
+    if (!qmm_narrow(M, N, K, bits, batch, 1, cus)) return false;
     // 16-column tiles where they fit one round, else 32-column tiles
     const long long t16 = (long long)((N + 15) / 16) * batch;
     const bool cols16 = t16 <= cus;
+    if (gs < 64 && !cols16) return false;
     const long long tiles = cols16 ? t16 : (long long)((N + 31) / 32) * batch;
     if (4 * tiles < cus || tiles > 2LL * cus || (tiles > cus && K / 512 > 10)) return false;
     const long long wide = (long long)((N + QMM_BN - 1) / QMM_BN) * batch;
@@ -95,7 +100,7 @@ bool qmm_narrow_preferred(int M, int N, int K, int bits, int gs, long long batch
     // M = 4..32: within 3% of the best route where the blocks are close)
     const double narrow_blocks = (double)((tiles + cus - 1) / cus) * (K / 512) * (cols16 ? 0.7 : 1.0);
     const long long split_blocks = (wide_tiles * s + cus - 1) / cus * (K / (QMM_KB * s));
-    return narrow_blocks <= (double)split_blocks + 6.0;
+    return narrow_blocks <= (double)split_blocks + (gs < 64 ? 2.0 : 6.0);
 }
 
 hipError_t launch_qmm_t(const uint32_t* w, const void* s, const void* b, const void* x, void* out,

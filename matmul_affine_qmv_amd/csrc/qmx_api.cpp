@@ -114,7 +114,8 @@ bool small_m_prefers_matrix(int M, int N, int K, int bits, int gs, int batch, in
     if (M < 2 || M >= 8) return false;
     const int b = batch > 0 ? batch : 1;
     const double mcodes = (double)N * K * b / 1e6;
-    const bool narrow = qmx::qmm_narrow_preferred(M, N, K, bits, gs, b, cus);
+    // the M = 2..7 estimates below were fitted at gs 64 and 128
+    const bool narrow = gs >= 64 && qmx::qmm_narrow_preferred(M, N, K, bits, gs, b, cus);
     if (narrow && (long long)((N + 15) / 16) * b <= cus) {
         if (M >= 3) return true;
         return 3.4 + 0.8 * K / 1024.0 < std::max(2.5 + 0.16 * mcodes, 2.5 + 0.65 * K / 1024.0);

@@ -228,9 +228,15 @@ def test_plan_narrow_tiles_take_2_4_8_bit_codes():
     for bits in (2, 8):
         assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t", 1)
         assert qmx.plan(16, 4096, 4096, bits, 128, BF16, num_cus=256) == ("qmm_t", 1)
-    for bits in (2, 4, 8):   # gs 32: two group epilogues per wave and block; the split plan stays,
-        # on 64 64-column tiles x 4 partitions
-        assert qmx.plan(16, 4096, 4096, bits, 32, BF16, num_cus=256) == ("qmm_t_splitk", 4)
+    for bits in (2, 4, 8):   # gs 32: two group epilogues per wave and block; 16-column tiles
+        # within 2 blocks of the split plan (8 against 4 x 0.7 here)
+        assert qmx.plan(16, 4096, 4096, bits, 32, BF16, num_cus=256) == ("qmm_t", 1)
+    # ... and the split plan beyond that, or where 32-column tiles would be needed
+    assert qmx.plan(16, 2048, 2048, 4, 32, BF16, num_cus=256) == ("qmm_t", 1)       # 5.4 against 7.1 us
+    assert qmx.plan(16, 1024, 4096, 4, 32, BF16, num_cus=256) == ("qmm_t_splitk", 16)  # 7.3 against 7.8
+    assert qmx.plan(16, 4096, 8192, 4, 32, BF16, num_cus=256) == ("qmm_t_splitk", 4)   # 11.6 against 12.6
+    assert qmx.plan(16, 14336, 4096, 4, 32, BF16, num_cus=256) == ("qmm_t_splitk", 2)  # 16.3 against 19.8
+    assert qmx.plan(4, 4096, 4096, 4, 32, BF16, num_cus=256) == ("qmv", 1)   # M = 2..7 rule fitted at gs 64
     for bits in (1, 3, 5, 6):
         assert qmx.plan(16, 4096, 4096, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 8)
         assert qmx.plan(16, 4096, 1024, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 4)
