@@ -140,14 +140,14 @@ template <int DT, int BITS, int GS, int MT, int WK = 2, int NBT = QMM_NB>
 constexpr int qmm_sbv_chunks() { return QmmCfg<DT, BITS, GS, MT, true, WK, NBT>::SBV_CHUNKS; }
 
 // Bank spread of 2-, 4- and 8-bit W rows of SLOTS copy slots: slot p of row R
-// holds piece (or word) p ^ w_swz(R) of the row.  The 128-column rows (4, 8 and
-// 8 slots) XOR a few row bits above the ones a wave's lanes share; the 512-column
-// rows (16 or 32 slots) the low 4 bits of the row, so the 16 rows of a fragment
-// read distinct slots.
+// holds piece (or word) p ^ w_swz(R) of the row.  Rows of 4 or 8 16-byte slots
+// (64 or 128 bytes) XOR the row bits above the ones that already separate the
+// banks of a fragment's 16 rows (2 and 1 of them), so that those rows read
+// distinct banks; rows of 16 or more slots the low 4 bits of the row.
 template <int BITS, int SLOTS>
 __device__ __forceinline__ int w_swz(int R) {
     if constexpr (SLOTS >= 16) return R & 15;
-    else if constexpr (BITS == 4) return (R >> 2) & 3;
+    else if constexpr (BITS == 4) return SLOTS == 8 ? (R >> 1) & 7 : (R >> 2) & 3;
     else if constexpr (BITS == 8) return (R >> 1) & 7;
     else return (R >> 3) & 7;
 }
