@@ -58,11 +58,52 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
 // against 18.5, (4096, 4096, 64) 13.4 against 16.9, (4096, 4096, 128) 17.7
 // against 20.3, (5120, 5120, 48) 14.3 against 16.1; taken while the tiles of
 // all partitions fit one round of the chip (at twice that they lost 10-20%).
+// Chunks of staged scales and biases a 64-column work-group of MT row
+// fragments holds in LDS.
+template <int DT, int BITS, int GS>
+static int wide64_sbv_capacity(int mt) {
+    switch (mt) {
+        case 1: return qmm_sbv_chunks<DT, BITS, GS, 1, 4>();
+        case 2: return qmm_sbv_chunks<DT, BITS, GS, 2, 4>();
+        case 3: return qmm_sbv_chunks<DT, BITS, GS, 3, 4>();
+        default: return qmm_sbv_chunks<DT, BITS, GS, 4, 4>();
+    }
+}
+
+template <int DT, int BITS>
+static int wide64_sbv_capacity_gs(int gs, int mt) {
+    return gs == 32 ? wide64_sbv_capacity<DT, BITS, 32>(mt)
+         : gs == 64 ? wide64_sbv_capacity<DT, BITS, 64>(mt) : wide64_sbv_capacity<DT, BITS, 128>(mt);
+}
+
+template <int DT>
+static int wide64_sbv_capacity_bits(int bits, int gs, int mt) {
+    return bits == 2 ? wide64_sbv_capacity_gs<DT, 2>(gs, mt)
+         : bits == 4 ? wide64_sbv_capacity_gs<DT, 4>(gs, mt) : wide64_sbv_capacity_gs<DT, 8>(gs, mt);
+}
+
 bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus) {
     if ((bits != 2 && bits != 4 && bits != 8) || K % 256 != 0 || M < 1 || M > 192 || splits < 2 || cus <= 0)
         return false;
     const long long tiles = (long long)((N + 63) / 64) * ((M + 63) / 64) * batch;
     return tiles * splits <= cus;
+}
+
+// Without staged scales and biases each stage carries its block's raw values,
+// which cost more than the 128-column plan's extra partitions (8-bit codes at
+// (17408, 5120, 56): 38.1 us on 64-column tiles in 3 partitions without them,
+// 36.8 us on 128-column tiles in 6 with them); at a given partition count the
+// 64-column tiles stay ahead either way (twice the work-groups).
+bool qmm_wide64_staged(int M, int K, int bits, int gs, int dt, int splits) {
+    if ((bits != 2 && bits != 4 && bits != 8) || (gs != 32 && gs != 64 && gs != 128) ||
+        (dt != DT_F16 && dt != DT_BF16) || K % 256 != 0 || M < 1 || M > 192 || splits < 1)
+        return false;
+    if ((K / gs) % 8 != 0) return true;   // staged on neither tile width
+    const int mt = qmm_mt_for(M, (M + 63) / 64);
+    const int groups = (K / 256 + splits - 1) / splits * (256 / gs);
+    const int cap = dt == DT_F16 ? wide64_sbv_capacity_bits<DT_F16>(bits, gs, mt)
+                                 : wide64_sbv_capacity_bits<DT_BF16>(bits, gs, mt);
+    return (groups + 7) / 8 + 2 <= cap;
 }
 
 // A narrow work-group walks all of K (K / 512 blocks) where each partition of

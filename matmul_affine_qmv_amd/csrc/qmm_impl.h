@@ -106,8 +106,12 @@ struct QmmCfg {
     static constexpr int SBPT = SBV ? 0 : (SB_VALUES + QMM_THREADS - 1) / QMM_THREADS;
     static constexpr int SB_BYTES = SBPT * QMM_THREADS * 4;
     static constexpr int STAGE = X_BYTES + W_BYTES + SB_BYTES;
-    // ring depth: up to 4 stages, leaving SBV at least 12 KB for its chunks
-    static constexpr int RING_LDS = 160 * 1024 - (SBV ? 12 * 1024 : 0);
+    // ring depth: up to 4 stages, leaving SBV at least 12 KB for its chunks; the
+    // 64-column tiles (split partitions twice as long as on 128-column tiles)
+    // leave room for 12 chunks where three stages still fit
+    static constexpr int RING_W4 = 160 * 1024 - 12 * 2 * BN * 16;
+    static constexpr int RING_LDS = (SBV && WK == 4 && RING_W4 / STAGE >= 3) ? RING_W4
+                                  : 160 * 1024 - (SBV ? 12 * 1024 : 0);
     static constexpr int NS = RING_LDS / STAGE < 4 ? RING_LDS / STAGE : 4;
     static constexpr int LPS = XPT + WPT + SBPT;              // copies per thread per stage
     static constexpr int LPS_NW = XPT + SBPT;                 // ... in waves that copy no W
@@ -701,8 +705,10 @@ hipError_t qmm_launch_mt(const uint32_t* w, const void* s, const void* b, const 
     // Staged scales/biases need 16-byte aligned arrays, rows of whole 16-byte chunks
     // (K/GS a multiple of 8) and a K range whose chunks (plus one for alignment and
     // one for an odd count) fit the LDS left over.
-    const int G = K / GS, nkb = K / C::KB;
-    const int nk_max = (nkb + splits - 1) / splits;
+    // the longest partition: whole segments of 256 columns (128 when K is not a
+    // multiple of 256), ceil(nseg / splits) of them
+    const int G = K / GS, seg = (K & 255) == 0 ? 256 : 128;
+    const int nk_max = (K / seg + splits - 1) / splits * seg / C::KB;
     const bool aligned = ((reinterpret_cast<uintptr_t>(s) | reinterpret_cast<uintptr_t>(b)) & 15) == 0 &&
                          (sd.sb * 2) % 16 == 0;
     const bool sbv = aligned && K > 0 && G % 8 == 0 &&

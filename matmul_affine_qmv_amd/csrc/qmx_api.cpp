@@ -147,11 +147,14 @@ int plan_impl(int M, int N, int K, int bits, int gs, int dtype, int num_cus, int
     const long long tiles = col_tiles * qmx::qmm_mtiles_for(M, col_tiles, num_cus, K);
     int s = qmx::qmm_policy_splits(tiles, K, num_cus);
     // where 64-column tiles take the split partitions, as many partitions as keep
-    // those resident at once (about half the 128-column plan's)
+    // those resident at once (about half the 128-column plan's), while they can
+    // stage the partition's scales and biases
     if ((bits == 2 || bits == 4 || bits == 8) && K % 256 == 0 && M <= 192) {
         const long long tiles64 = (long long)((N + 63) / 64) * ((M + 63) / 64) * batch;
         const int s64 = qmx::qmm_policy_splits(tiles64, K, num_cus);
-        if (s64 >= 2 && qmx::qmm_wide64(M, N, K, bits, batch, s64, num_cus)) s = s64;
+        if (s64 >= 2 && qmx::qmm_wide64(M, N, K, bits, batch, s64, num_cus) &&
+            qmx::qmm_wide64_staged(M, K, bits, gs, dtype, s64))
+            s = s64;
     }
     if (s >= 2 && qmx::qmm_narrow_preferred(M, N, K, bits, gs, batch, num_cus)) s = 1;
     *route = s >= 2 ? QMX_ROUTE_QMM_T_SPLITK : QMX_ROUTE_QMM_T;

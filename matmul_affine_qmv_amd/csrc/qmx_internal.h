@@ -38,8 +38,13 @@ int qmm_mt_for(int M, int mtiles);
 // tiles that would leave some of the `cus` compute units idle, and at most
 // 3 * cus narrow tiles.
 bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int cus);
-// Split-K partitions run on 64-column tiles of 256-column blocks.
+// Whether `splits` split-K partitions run on 64-column tiles of 256-column
+// blocks: 2-, 4- or 8-bit codes, K a multiple of 256, M <= 192 and the tiles of
+// all partitions within one round of the `cus` compute units.
 bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus);
+// Whether such a 64-column work-group can stage the longest partition's scales
+// and biases in LDS (or neither tile width can: K / gs not a multiple of 8).
+bool qmm_wide64_staged(int M, int K, int bits, int gs, int dt, int splits);
 // Whether the dispatch policy runs such a problem unsplit on 32-column tiles
 // rather than split-K on 128-column tiles: the narrow tiles launch between a
 // quarter of the compute units and all of them, K is short enough for one

@@ -244,6 +244,19 @@ def test_plan_narrow_tiles_take_2_4_8_bit_codes():
     assert qmx.plan(16, 4096, 1152, 4, 64, BF16, num_cus=256)[0] == "qmm_t_splitk"
 
 
+def test_plan_64_column_split_needs_staged_scales():
+    """64-column split tiles take half the partitions only where their LDS holds
+    the longest partition's scales and biases: at (17408, 5120, 56) the 8-bit
+    work-group has room for 6 chunks, the partition needs 14, so the 128-column
+    plan (6 partitions) stays; 2- and 4-bit work-groups hold 15."""
+    assert qmx.plan(56, 5120, 17408, 8, 64, BF16, num_cus=256) == ("qmm_t_splitk", 6)
+    for bits in (2, 4):
+        assert qmx.plan(56, 5120, 17408, bits, 64, BF16, num_cus=256) == ("qmm_t_splitk", 3)
+    assert qmx.plan(56, 5120, 17408, 4, 32, F16, num_cus=256) == ("qmm_t_splitk", 6)   # 23 chunks at gs 32
+    assert qmx.plan(128, 4096, 4096, 8, 64, BF16, num_cus=256) == ("qmm_t_splitk", 2)  # 4 + 2 chunks fit
+    assert qmx.plan(85, 2048, 10752, 8, 64, BF16, num_cus=256) == ("qmm_t_splitk", 4)
+
+
 def test_plan_respects_split_limits():
     for K in (512, 768, 1024, 2048, 14336):
         for N in (128, 1024, 4096):
