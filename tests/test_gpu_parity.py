@@ -502,6 +502,8 @@ def _strided(x, kind):
     (3, 85, 128, 2560, 5, 32, qi.BF16, False, "odd"),          # two M tiles, split-K, odd offset
     (6, 16, 1024, 2048, 4, 64, qi.BF16, False, "padded"),      # 32-column tiles across the batch
     (4, 25, 2048, 1024, 4, 128, qi.F16, True, "odd"),          # 32-column tiles, shared weights, x copied first
+    (3, 40, 512, 2048, 8, 64, qi.BF16, True, "padded"),        # 64-column split tiles, shared weights
+    (2, 150, 256, 3072, 2, 128, qi.F16, False, "contiguous"),  # 64-column split tiles, three 64-row tiles
 ])
 def test_batched_strided_and_odd_offset(orc, B, M, N, K, bits, gs, dt, shared, layout):
     route = qmx.plan_batched(B, M, N, K, bits, gs, dt, 256)
