@@ -15,7 +15,11 @@ bfloat16 path the metric is quoted on:
 Whole steps: R distinct input sets rotate from step to step so that at least
 three times the 256 MB Infinity Cache is touched between two uses of a set;
 each set's step is captured once in a HIP graph and replayed (no host launch
-cost); `value` is algorithmic bytes per second over the K timed steps.
+cost); `value` is algorithmic bytes per second over the K timed steps.  The
+calls' split-K workspaces (scratch, not inputs) are one buffer shared by all
+calls and sets.  Before the timed steps come the W warm-up steps of every set
+and then more untimed replays until the GPU has been busy for 50 ms, since
+its clock ramps up over the first milliseconds of load.
 
 Per call and per kernel: every call gets its own rotation of distinct input
 sets totalling at least 512 MiB (twice the Infinity Cache), so no call is
@@ -125,6 +129,7 @@ WORKLOADS = {
     "blocks_14336x5120": [block("q8_0", 14336, 5120), block("q4_k", 14336, 5120)],
 }
 DEFAULT_WORKLOAD = "qmv_qmm_4bit_gs64_bf16"
+SETTLE_S = 0.05   # seconds of untimed step replays before the timed steps
 
 
 def call_name(c):
@@ -619,6 +624,16 @@ def main(argv=None):
     nsets = max(3, math.ceil(3 * MALL_BYTES / per_set))
     sets = [set0] + [[make_inputs(c, args.seed + 104729 * r + 7919 * i, dev) for i, c in enumerate(calls)]
                      for r in range(1, nsets)]
+    # the split-K partials of every call and set go to one scratch workspace, as a
+    # runtime's scratch arena would hold them (the per-call rotations below share
+    # set 0's the same way); the calls run in order on one stream
+    ws_need = max((d["ws"].numel() for s in sets for d in s if d.get("ws") is not None), default=0)
+    if ws_need:
+        scratch = torch.empty(ws_need, dtype=torch.float32, device=dev)
+        for s in sets:
+            for d in s:
+                if d.get("ws") is not None:
+                    d["ws"] = scratch[: d["ws"].numel()]
     torch.cuda.synchronize()
 
     # eager warm-up (loads code objects, caches the CU count), then capture one graph per set
@@ -627,7 +642,14 @@ def main(argv=None):
             launch(c, d)
     torch.cuda.synchronize()
     graphs = [capture(lambda s=s: [launch(c, d) for c, d in zip(calls, s)]) for s in sets]
-    time_graphs(graphs, max(args.warmup, 1) * len(graphs))
+    warm = max(args.warmup, 1) * len(graphs)
+    t_warm, _ = time_graphs(graphs, warm)
+    # more untimed replays until the GPU has been busy for SETTLE_S, so that its
+    # clock has ramped up before the timed steps (50 steps of the default
+    # workload measured 3-5% slower per step than 200 without this)
+    extra = math.ceil(max(0.0, SETTLE_S - t_warm) / (t_warm / warm))
+    if extra:
+        time_graphs(graphs, extra)
     say(f"{len(calls)} calls, {nsets} step sets of {per_set / 1e6:.1f} MB; timing {args.steps} steps")
     wall, gpu_ms = time_graphs(graphs, args.steps)
     step_bytes = sum(alg_bytes(c) for c in calls)
