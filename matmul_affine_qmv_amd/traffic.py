@@ -142,6 +142,35 @@ def counters_markdown(run_dirs, substring: str, exclude: str = "") -> str:
     return "\n".join(out) + "\n"
 
 
+def timeline_markdown(trace_csv: str, per_step: int, steps: int, substring: str = "qmx::") -> str:
+    """Per position of a replayed step: the median duration of its kernel and
+    the median gap from the previous kernel's end, over the last `steps` steps
+    of a --kernel-trace run (each step `per_step` library kernels in order)."""
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if substring in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                             r["Kernel_Name"].split("(")[0].replace("void ", "")))
+    rows.sort()
+    last = rows[-per_step * steps:]
+    if len(last) < per_step * steps:
+        raise SystemExit(f"{trace_csv}: fewer than {per_step * steps} library kernels")
+    out = ["| position | kernel | duration µs (median) | gap before it µs (median) |", "|---:|---|---:|---:|"]
+    for i in range(per_step):
+        ks = [last[per_step * j + i] for j in range(steps)]
+        dur = statistics.median((e - b) / 1e3 for b, e, _ in ks)
+        gaps = [(last[per_step * j + i][0] - last[per_step * j + i - 1][1]) / 1e3
+                for j in range(steps) if per_step * j + i > 0]
+        out.append(f"| {i} | `{ks[0][2]}` | {dur:.2f} | {statistics.median(gaps) if gaps else 0.0:.2f} |")
+    span = statistics.median((last[per_step * j + per_step - 1][1] - last[per_step * j][0]) / 1e3 for j in range(steps))
+    busy = statistics.median(sum((e - b) / 1e3 for b, e, _ in last[per_step * j:per_step * (j + 1)])
+                             for j in range(steps))
+    out += ["", f"Step span (first kernel's start to last kernel's end, median): {span:.1f} µs; "
+            f"sum of its kernels' durations: {busy:.1f} µs."]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -162,7 +191,14 @@ def main(argv=None) -> int:
     k.add_argument("dirs", nargs="+", help="one rocprofv3 output directory per pass")
     k.add_argument("--kernel", required=True, help="substring of the kernel name to keep")
     k.add_argument("--exclude", default="", help="substring of kernel names to drop")
+    tl = sub.add_parser("timeline", help="per-position kernel durations and gaps of a replayed step")
+    tl.add_argument("csv", help="run_kernel_trace.csv")
+    tl.add_argument("--per-step", type=int, required=True, help="library kernels per step")
+    tl.add_argument("--steps", type=int, required=True, help="the last N steps of the trace")
     args = ap.parse_args(argv)
+    if args.cmd == "timeline":
+        print(timeline_markdown(args.csv, args.per_step, args.steps), end="")
+        return 0
     if args.cmd == "stats":
         print(kernel_stats_markdown(args.csv), end="")
         return 0
