@@ -230,7 +230,10 @@ int qmx_matvec_q8_i8(const uint32_t* wq, const uint32_t* xq, const float* wd, fl
  * otherwise qmx_qmm_t, split along K when its tiles leave compute units idle
  * (tiles of 128 columns by up to 64 rows of x; above M = 192 by up to 128
  * rows when those fill the device or launch more work-groups after the
- * split).  Performs no HIP call.  Returns QMX_OK or a validation status.
+ * split; for 2-, 4- and 8-bit codes split tiles of 64 columns at half the
+ * partitions where they fit one round of the device, and unsplit tiles of
+ * 16 or 32 columns for M <= 32 where few columns would leave compute units
+ * idle).  Performs no HIP call.  Returns QMX_OK or a validation status.
  * route/splits: host pointers.
  */
 int qmx_plan(int M, int N, int K, int bits, int group_size, int dtype, int num_cus,
