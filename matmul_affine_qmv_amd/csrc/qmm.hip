@@ -58,6 +58,13 @@ bool qmm_narrow(int M, int N, int K, int bits, long long batch, int splits, int 
 // against 18.5, (4096, 4096, 64) 13.4 against 16.9, (4096, 4096, 128) 17.7
 // against 20.3, (5120, 5120, 48) 14.3 against 16.1; taken while the tiles of
 // all partitions fit one round of the chip (at twice that they lost 10-20%).
+bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus) {
+    if ((bits != 2 && bits != 4 && bits != 8) || K % 256 != 0 || M < 1 || M > 192 || splits < 2 || cus <= 0)
+        return false;
+    const long long tiles = (long long)((N + 63) / 64) * ((M + 63) / 64) * batch;
+    return tiles * splits <= cus;
+}
+
 // Chunks of staged scales and biases a 64-column work-group of MT row
 // fragments holds in LDS.
 template <int DT, int BITS, int GS>
@@ -80,13 +87,6 @@ template <int DT>
 static int wide64_sbv_capacity_bits(int bits, int gs, int mt) {
     return bits == 2 ? wide64_sbv_capacity_gs<DT, 2>(gs, mt)
          : bits == 4 ? wide64_sbv_capacity_gs<DT, 4>(gs, mt) : wide64_sbv_capacity_gs<DT, 8>(gs, mt);
-}
-
-bool qmm_wide64(int M, int N, int K, int bits, long long batch, int splits, int cus) {
-    if ((bits != 2 && bits != 4 && bits != 8) || K % 256 != 0 || M < 1 || M > 192 || splits < 2 || cus <= 0)
-        return false;
-    const long long tiles = (long long)((N + 63) / 64) * ((M + 63) / 64) * batch;
-    return tiles * splits <= cus;
 }
 
 // Without staged scales and biases each stage carries its block's raw values,
