@@ -123,6 +123,12 @@ WORKLOADS = {
                                      for c in [affine("qmm", m, n, k), affine("qmv", m, n, k), affine("qmm_t", m, n, k)]
                                      + [affine("splitk", m, n, k, splits=s) for s in (2, 4, 8)
                                         if k // 256 >= s and (n + 127) // 128 * s <= 512]],
+    # group size 32 at M = 8..32: the unsplit narrow tiles against the split plans, and the policy's pick
+    "route_narrow_gs32_4bit_bf16": [c for n, k in ((4096, 4096), (2048, 2048), (1024, 4096), (4096, 8192), (14336, 4096))
+                                    for m in (8, 16, 32)
+                                    for c in [affine("qmm", m, n, k, gs=32), affine("qmm_t", m, n, k, gs=32)]
+                                    + [affine("splitk", m, n, k, gs=32, splits=s) for s in (2, 4, 8, 16)
+                                       if k // 256 >= s]],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
     "q8_i8_14336x5120": [block("q8_i8", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
