@@ -129,6 +129,13 @@ WORKLOADS = {
                                     for c in [affine("qmm", m, n, k, gs=32), affine("qmm_t", m, n, k, gs=32)]
                                     + [affine("splitk", m, n, k, gs=32, splits=s) for s in (2, 4, 8, 16)
                                        if k // 256 >= s]],
+    # split counts 2-8 of 2-, 4- and 8-bit codes at the config-3 split shapes and three more M: a
+    # count runs on 64-column tiles where those of all its partitions fit one round, else 128-column
+    "route_split_tiles_bf16": [c for b in (2, 4, 8) for k, n, m in ((17408, 5120, 56), (14336, 4096, 33),
+                                                                      (10752, 2048, 85), (4096, 4096, 64),
+                                                                      (4096, 4096, 128), (5120, 5120, 48))
+                               for c in [affine("qmm", m, n, k, bits=b)]
+                               + [affine("splitk", m, n, k, bits=b, splits=s) for s in (2, 3, 4, 6, 8)]],
     "q8_0_14336x5120": [block("q8_0", 14336, 5120)],
     "q8_i8_14336x5120": [block("q8_i8", 14336, 5120)],
     "q4_k_14336x5120": [block("q4_k", 14336, 5120)],
